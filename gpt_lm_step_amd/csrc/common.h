@@ -1,0 +1,123 @@
+// Internal helpers shared by the gfx950 kernels of libgpt: element types, vector loads,
+// 64-wide wavefront reductions and the host-side status plumbing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/gpt.h"
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int WAVE = 64;
+
+// ------------------------------------------------------------------ element helpers
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// Eight consecutive elements of T as one vector register group (16 B for bf16, 32 B for f32).
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> { typedef bf16x8 type; };
+template <> struct Vec8<float> { typedef f32x8 type; };
+template <typename T> using vec8_t = typename Vec8<T>::type;
+
+template <typename T>
+__device__ __forceinline__ vec8_t<T> load8(const T* p) {
+  return *reinterpret_cast<const vec8_t<T>*>(p);
+}
+template <typename T>
+__device__ __forceinline__ void store8(T* p, vec8_t<T> v) {
+  *reinterpret_cast<vec8_t<T>*>(p) = v;
+}
+template <typename T>
+__device__ __forceinline__ void load8_f32(const T* p, float* out) {
+  vec8_t<T> v = load8(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = to_f32(v[i]);
+}
+template <typename T>
+__device__ __forceinline__ void store8_f32(T* p, const float* in) {
+  vec8_t<T> v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = from_f32<T>(in[i]);
+  store8(p, v);
+}
+
+// ------------------------------------------------------------------ wave reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int o = width >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+// Block-wide sum for blockDim.x a multiple of 64 (<= 1024); result valid in every thread.
+__device__ __forceinline__ float block_sum(float v, float* smem /* >= 16 floats */) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE, nw = blockDim.x / WAVE;
+  __syncthreads();
+  if (l == 0) smem[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += smem[i];
+  return t;
+}
+__device__ __forceinline__ float block_max(float v, float* smem) {
+  v = wave_max(v);
+  const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE, nw = blockDim.x / WAVE;
+  __syncthreads();
+  if (l == 0) smem[w] = v;
+  __syncthreads();
+  float t = -INFINITY;
+  for (int i = 0; i < nw; ++i) t = fmaxf(t, smem[i]);
+  return t;
+}
+
+// ------------------------------------------------------------------ host plumbing
+namespace gpt {
+
+void set_error(const std::string& msg);
+gpt_status fail(gpt_status s, const std::string& msg);
+gpt_status check_launch(const char* what);
+
+inline unsigned cdiv(long long a, long long b) { return (unsigned)((a + b - 1) / b); }
+inline size_t align_up(size_t n, size_t a = 256) { return (n + a - 1) / a * a; }
+
+// Bump allocator over a caller-provided workspace.  With base == nullptr it only measures
+// (size() is then the bytes a real carve needs).
+struct Carver {
+  char* base;
+  size_t cap, off = 0;
+  bool ok = true;
+  Carver(void* b, size_t c) : base((char*)b), cap(c) {}
+  template <typename T>
+  T* take(size_t n) {
+    size_t at = align_up(off);
+    off = at + n * sizeof(T);
+    if (base == nullptr) return nullptr;
+    if (off > cap) { ok = false; return nullptr; }
+    return (T*)(base + at);
+  }
+  size_t size() const { return align_up(off); }
+};
+
+}  // namespace gpt

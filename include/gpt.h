@@ -1,0 +1,163 @@
+/*
+ * gpt.h -- C ABI of libgpt.so: one training step (forward + hand-written backward) of a
+ * GPT-style decoder, and the hashed n-gram tables with their inlined sparse optimizer, on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (definitions from the pages; each entry point cites its own):
+ *   - the decoder of the "$1000 tier nanochat run" discussion (nanochat #8, the GPT class a
+ *     commenter posted): x = norm(wte[idx]); per block x += attn(norm(x)), x += mlp(norm(x));
+ *     norm(x); untied lm_head; logits softcap 15*tanh(z/15); mean cross-entropy over targets
+ *     != -1.  norm is RMSNorm without weight (modded-nanogpt README: "Removed all affine scale
+ *     and bias parameters"), attention has half-split rotary embeddings, QK-norm and a causal
+ *     mask, the MLP activation is ReLU^2 (README: "ReLU^2 activation").
+ *   - the decoder-rtx tables (Chris McCormick posts, baseline-4 thread): a hashed bigram row
+ *     added to x0, a hashed bigram row and a projected frozen trigram row added to the
+ *     attention values, and a sparse optimizer "with no first moment and only per-row
+ *     magnitude" applied inside backward so that no table-gradient buffer exists.
+ *
+ * Conventions (all entry points):
+ *   - Pointers are DEVICE pointers unless marked [host].  All memory is caller-owned; the
+ *     library never allocates device memory and never synchronises the stream, except where a
+ *     function says so.  Every launch is ordered on the stream argument.
+ *   - Row-major everywhere.  Activations are token-major [N, .] with N = batch * seq_len,
+ *     token (b, t) at row b * seq_len + t.  Weights are [out, in] (nn.Linear layout).
+ *   - Arguments are validated before any launch; a failing call returns a negative status
+ *     and launches nothing.  Launch failures return GPT_EHIP.  gpt_last_error() [host] gives
+ *     a human-readable message for the last failure on the calling thread.
+ *   - bf16 means IEEE bfloat16 storage; all bf16 stores round to nearest even from fp32.
+ */
+#ifndef GPT_H_
+#define GPT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPT_OK = 0,
+  GPT_EINVAL = -1,      /* null pointer, bad enum, unsupported option */
+  GPT_ESHAPE = -2,      /* a size or alignment the kernels do not support */
+  GPT_ERANGE = -3,      /* a value out of range (detected on the host) */
+  GPT_EWORKSPACE = -4,  /* workspace missing or smaller than the query said */
+  GPT_EHIP = -5         /* a HIP launch or runtime call failed */
+} gpt_status;
+
+typedef enum { GPT_F32 = 0, GPT_BF16 = 1 } gpt_dtype;
+
+/* Model configuration.  d_model = n_head * head_dim; n_kv_head must equal n_head (every
+ * configuration on the pages uses as many key/value heads as query heads).
+ * Supported: head_dim in {32, 64, 128}; d_model, d_mlp and vocab multiples of 64;
+ * seq_len a multiple of 64; dtype GPT_BF16 (bf16 storage, fp32 accumulation, fp32 residual
+ * stream and gradients) or GPT_F32 (everything fp32). */
+typedef struct {
+  int32_t n_layer, d_model, n_head, n_kv_head, head_dim, d_mlp, vocab, seq_len, batch;
+  int32_t dtype;       /* gpt_dtype of parameters, activations and table addends */
+  float rms_eps;       /* RMSNorm epsilon inside the square root (1e-6) */
+  float rope_base;     /* rotary base (10000) */
+  float softcap;       /* logit softcap c = s*tanh(z/s); 0 disables (15) */
+  int32_t qk_norm;     /* 1: RMSNorm q and k per head after the rotation */
+  int32_t has_x0_add;  /* 1: a per-token addend is added to x0 (after the embedding norm) */
+  int32_t has_v_add;   /* 1: a per-token addend is added to the values of every layer */
+  int32_t has_trigram; /* 1: gathered trigram rows, projected by wtri [D,D], add to values */
+} gpt_config;
+
+/* One entry of the flat parameter layout. */
+typedef struct {
+  char name[48];        /* "wte", "h<l>.wqkv", "h<l>.wo", "h<l>.wfc", "h<l>.wpr", "lm_head", "wtri" */
+  int64_t offset_elems; /* offset in elements into the flat buffer (a multiple of 64) */
+  int32_t ndim;         /* always 2 */
+  int64_t shape[2];     /* [rows, cols]; h<l>.wqkv stacks the q, k and v projections [3D, D] */
+} gpt_tensor_desc;
+
+typedef struct gpt_ctx gpt_ctx;
+
+/* Flat parameter layout of `cfg` [host, no GPU work].  Order: wte [V,D]; per layer l:
+ * h<l>.wqkv [3D,D], h<l>.wo [D,D], h<l>.wfc [F,D], h<l>.wpr [D,F]; lm_head [V,D]; wtri [D,D]
+ * if has_trigram.  `out` may be NULL to query the count; otherwise it must hold *count
+ * entries on entry ([host] in/out: capacity in, number written out).  `total_elems` [host,
+ * optional] receives the flat buffer length.  The gradient buffer uses the same layout. */
+gpt_status gpt_param_layout(const gpt_config* cfg, gpt_tensor_desc* out, int32_t* count,
+                            int64_t* total_elems);
+
+/* Device workspace, in bytes, that gpt_init needs for `cfg` [host].  It holds the activation
+ * stash of every layer, the logits of the LM head, rotary tables and sort scratch. */
+gpt_status gpt_workspace_bytes(const gpt_config* cfg, size_t* bytes);
+
+/* Create a step context over a caller-provided workspace (256-byte aligned, at least
+ * gpt_workspace_bytes).  Enqueues one kernel on `stream` that fills the rotary tables
+ * (cos/sin of t * base^(-2i/head_dim), stored in `dtype`, as _precompute_rotary_embeddings
+ * on the nanochat page).  *out [host] receives the context.  Not thread-safe per context. */
+gpt_status gpt_init(const gpt_config* cfg, void* workspace, size_t ws_bytes, hipStream_t stream,
+                    gpt_ctx** out);
+
+/* One forward + backward pass (GPT.forward on the nanochat page, then the chain rule).
+ *   tokens   int32 [B,T]: input ids; targets int32 [B,T]: next-token ids, -1 = ignored.
+ *            Ids outside [0, vocab) are clamped for addressing and reported by
+ *            gpt_check_errors (they never fault).
+ *   params   flat buffer in `dtype` per gpt_param_layout (read only).
+ *   grads    flat fp32 buffer, same layout: the gradient of grad_scale * loss.  accumulate = 0
+ *            overwrites every entry; accumulate = 1 adds to it (gradient accumulation).
+ *   x0_add, v_add, tri_rows  [N,D] in `dtype`: gathered table rows (bigram_fwd with y = 0),
+ *            required iff has_x0_add / has_v_add / has_trigram, else ignored.
+ *            The value addend is u = v_add + tri_rows * wtri^T, added to v in every layer.
+ *   d_x0_add, d_v_add  [N,D] in `dtype` (may be NULL): per-token gradients of
+ *            grad_scale * loss w.r.t. x0_add and v_add (u), always overwritten.  These feed
+ *            bigram_bwd_update; no [rows, D] table gradient exists anywhere.
+ *   loss     fp32 device scalar: mean cross-entropy over valid targets (not scaled).
+ * Stream-ordered; never synchronises. */
+gpt_status gpt_fwd_bwd(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
+                       const void* params, float* grads, float grad_scale, int32_t accumulate,
+                       const void* x0_add, const void* v_add, const void* tri_rows,
+                       void* d_x0_add, void* d_v_add, float* loss, hipStream_t stream);
+
+/* Bit flags of problems the kernels of this context detected since the last call:
+ * 1 = an input token id outside [0, vocab); 2 = a target id outside [-1, vocab).  The
+ * offending ids were clamped (inputs) or ignored (targets), so nothing faulted.
+ * Synchronises `stream`, then clears the flags.  flags [host]. */
+gpt_status gpt_check_errors(gpt_ctx* ctx, hipStream_t stream, int32_t* flags);
+
+gpt_status gpt_destroy(gpt_ctx* ctx);
+
+/* Hashed n-gram gather-add (decoder-rtx bigram/trigram tables).  For each sequence b and
+ * position t with current id c = tokens[b,t], previous ids p = tokens[b,t-1], pp = tokens[b,t-2]
+ * (a missing previous id is `vocab`):
+ *   order 2: h = (p * 1000003 + c) mod rows;  order 3: h = ((pp * 1000003 + p) * 1000003 + c) mod rows
+ * in exact 64-bit integer arithmetic (ids are read as unsigned 32-bit values), then
+ *   y[b*T+t, :] += table[h, :]   (fp32 add, one rounding to `dtype`).
+ * tokens int32 [B,T]; table [rows, dim] and y [B*T, dim] in `dtype`; h_out int32 [B*T] or
+ * NULL.  Requires dim % 8 == 0, 1 <= rows < 2^31, order in {2, 3}. */
+gpt_status bigram_fwd(const int32_t* tokens, int32_t B, int32_t T, int32_t order, int32_t vocab,
+                      const void* table, int64_t rows, int32_t dim, int32_t dtype, void* y,
+                      int32_t* h_out, hipStream_t stream);
+
+/* Device workspace in bytes for bigram_bwd_update over n tokens of width dim [host]. */
+size_t bigram_workspace_bytes(int64_t n, int32_t dim, int64_t rows);
+
+/* Sparse table update inlined in the tables' backward (decoder-rtx: no first moment, one
+ * magnitude per row, no .grad buffer).  For every row r hit by h (rows never hit are left
+ * bit-identical):
+ *   g_r = sum over t with h[t] == r of dy[t, :]    (fp32, in ascending t: deterministic)
+ *   v[r] = beta2 * v[r] + (1 - beta2) * mean_j g_r[j]^2
+ *   table[r, :] -= lr * g_r / (sqrt(v[r]) + eps)   (uses the new v[r])
+ * h int32 [n] (entries outside [0, rows) are skipped); dy [n, dim] in `dtype`; table
+ * [rows, dim] in `dtype` and v fp32 [rows] updated in place.  workspace: at least
+ * bigram_workspace_bytes(n, dim, rows) bytes, 256-byte aligned.  Requires dim % 8 == 0,
+ * n < 2^31.  n == 0 is a no-op. */
+gpt_status bigram_bwd_update(const int32_t* h, const void* dy, int64_t n, int32_t dim,
+                             int32_t dtype, void* table, float* v, int64_t rows, float lr,
+                             float beta2, float eps, void* workspace, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* Message for the last failing call on this thread [host]; never NULL. */
+const char* gpt_last_error(void);
+const char* gpt_status_string(gpt_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT_H_ */

@@ -1,0 +1,75 @@
+/*
+ * gpt_kernels.h -- per-kernel entry points of libgpt.so, for checking each stage of the step
+ * on its own.  They run exactly the kernels gpt_fwd_bwd launches, on caller buffers.
+ * Conventions as in gpt.h: device pointers, caller-owned memory, stream-ordered, validated
+ * before launch, negative status on failure.  `dtype` is GPT_F32 or GPT_BF16 and applies to
+ * the arguments marked T; the others are fp32 or int32 as stated.
+ */
+#ifndef GPT_KERNELS_H_
+#define GPT_KERNELS_H_
+
+#include "gpt.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* C[m,n] (+)= sum_k A(m,k) B(n,k), fp32 C (ldc), T operands.  a_kc/b_kc = 1: element (r,k)
+ * at p[r*ld + k]; 0: at p[k*ld + r].  beta 0 overwrites C, 1 adds to it.  K, lda, ldb must be
+ * multiples of 8; a row-contiguous A (B) needs M (N) a multiple of 8.  This is the matrix-core
+ * GEMM behind every projection of the step (nn.Linear layers of the nanochat GPT class). */
+gpt_status gptk_gemm(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32_t N, int32_t K,
+                     const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
+                     int64_t ldc, int32_t beta, hipStream_t stream);
+
+/* RMSNorm without weight (`norm` of the nanochat GPT class): x fp32 [N,D] -> y T [N,D],
+ * rstd fp32 [N] = 1/sqrt(mean(x^2) + eps).  D a multiple of 64, at most 2048. */
+gpt_status gptk_rmsnorm_fwd(int32_t dtype, const float* x, void* y, float* rstd, int64_t N,
+                            int32_t D, float eps, hipStream_t stream);
+
+/* dx = dres + rstd * (dy - y * mean(dy * y)), y = x * rstd (dres may be NULL or equal dx);
+ * dx_t (T, optional) receives dx rounded to T.  x, rstd, dy, dres, dx fp32. */
+gpt_status gptk_rmsnorm_bwd(int32_t dtype, const float* x, const float* rstd, const float* dy,
+                            const float* dres, float* dx, void* dx_t, int64_t N, int32_t D,
+                            hipStream_t stream);
+
+/* Rotary tables (`_precompute_rotary_embeddings`): cos/sin T [T, hd/2] of t*base^(-2i/hd). */
+gpt_status gptk_rope_table(int32_t dtype, void* cos_t, void* sin_t, int32_t T, int32_t hd,
+                           float base, hipStream_t stream);
+
+/* In place on the q and k column blocks of qkv T [B*T, 3*H*hd]: half-split rotation
+ * (`apply_rotary_emb`) then, if qk_norm, RMSNorm per head; rstd_qk fp32 [B*T, 2H] (q heads
+ * then k heads). */
+gpt_status gptk_rope_qknorm_fwd(int32_t dtype, void* qkv, const void* cos_t, const void* sin_t,
+                                float* rstd_qk, int64_t N, int32_t T, int32_t H, int32_t hd,
+                                int32_t qk_norm, float eps, hipStream_t stream);
+
+/* Backward of the above, in place on the dq/dk blocks of dqkv, given the saved qkv output. */
+gpt_status gptk_rope_qknorm_bwd(int32_t dtype, void* dqkv, const void* qkv, const void* cos_t,
+                                const void* sin_t, const float* rstd_qk, int64_t N, int32_t T,
+                                int32_t H, int32_t hd, int32_t qk_norm, hipStream_t stream);
+
+/* Causal attention forward (F.scaled_dot_product_attention(is_causal=True) in the nanochat
+ * GPT class): qkv T [B*T, 3D] -> out T [B*T, D], lse2 fp32 [B, H, T] = log2 sum_s
+ * 2^(q.k_s * log2(e)/sqrt(hd)) (base-2 log-sum-exp of the scaled scores). */
+gpt_status gptk_attention_fwd(int32_t dtype, const void* qkv, void* out, float* lse2, int32_t B,
+                              int32_t T, int32_t H, int32_t hd, hipStream_t stream);
+
+/* Attention backward: dqkv T [B*T, 3D] receives dq, dk, dv; scratch fp32 [B*H*T]. */
+gpt_status gptk_attention_bwd(int32_t dtype, const void* qkv, const void* out, const void* dout,
+                              const float* lse2, float* scratch, void* dqkv, int32_t B,
+                              int32_t T, int32_t H, int32_t hd, hipStream_t stream);
+
+/* Softcapped cross-entropy forward + backward in place (GPT.forward's loss): z T [rows, V]
+ * (row stride ldz) is overwritten by dz = (softmax(c) - onehot) (1 - tanh^2(z/cap))
+ * * grad_scale / n_valid, c = cap tanh(z/cap) (cap 0: c = z); loss_rows fp32 [rows] gets
+ * logsumexp(c) - c[target] (0 for ignored targets).  n_valid: int32 device scalar.
+ * V a multiple of 64, at most 65536. */
+gpt_status gptk_softcap_ce(int32_t dtype, void* z, int64_t ldz, const int32_t* targets,
+                           int64_t rows, int32_t V, float cap, float grad_scale,
+                           const int32_t* n_valid, float* loss_rows, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT_KERNELS_H_ */

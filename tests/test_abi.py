@@ -1,0 +1,113 @@
+"""The C-ABI library loads, exports every declared symbol, and its host-side logic (layout,
+workspace sizing, argument validation) works without a GPU.  No kernel is launched here."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from gpt_lm_step_amd import binding as B
+from gpt_lm_step_amd import configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in ("gpt.h", "gpt_kernels.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", src, flags=re.M):
+            if m.group(1) not in ("if", "return", "sizeof"):
+                names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert set(B.EXPORTS) | set(B.KERNEL_EXPORTS) == declared
+    lib = B.lib()
+    for name in sorted(declared):
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("cfg", list(configs.PRESETS.values()), ids=list(configs.PRESETS))
+def test_param_layout_matches_python_layout(cfg):
+    got, total = B.gpt_param_layout(cfg)
+    want = configs.param_layout(cfg)
+    assert [(n, o, tuple(s)) for n, o, s in got] == [(n, o, tuple(s)) for n, o, s in want]
+    assert total == configs.param_elems(cfg)
+
+
+def test_d32_layout_counts_the_page_parameters():
+    got, _ = B.gpt_param_layout(configs.D32)
+    assert sum(s[0] * s[1] for _, _, s in got) == 1_879_048_192
+
+
+def test_workspace_sizes_are_plausible():
+    small = B.gpt_workspace_bytes(configs.TINY)
+    big = B.gpt_workspace_bytes(configs.D32)
+    assert 0 < small < 64 << 20
+    # d32 stashes ~1.2 GB of activations per layer plus 2 GB of bf16 logits
+    assert 30e9 < big < 80e9
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 48, B.GPT_ESHAPE), ("n_kv_head", 2, B.GPT_ESHAPE), ("vocab", 500, B.GPT_ESHAPE),
+    ("seq_len", 100, B.GPT_ESHAPE), ("dtype", 7, B.GPT_EINVAL), ("n_layer", 0, B.GPT_ESHAPE),
+    ("vocab", 65536 + 64, B.GPT_ESHAPE), ("d_model", 4096, B.GPT_ESHAPE),
+])
+def test_invalid_configs_are_rejected(field, value, status):
+    c = B.make_config(configs.TINY)
+    setattr(c, field, value)
+    if field == "head_dim":
+        c.n_head = 1
+        c.d_model = 48 * 1
+    b = C.c_size_t(0)
+    assert B.lib().gpt_workspace_bytes(C.byref(c), C.byref(b)) == status
+    assert len(B.lib().gpt_last_error()) > 0
+
+
+def test_init_rejects_missing_or_small_workspace():
+    c = B.make_config(configs.TINY)
+    h = C.c_void_p()
+    assert B.lib().gpt_init(C.byref(c), None, 0, None, C.byref(h)) == B.GPT_EWORKSPACE
+    # a fake, aligned, too-small "workspace" address: rejected before any use
+    assert B.lib().gpt_init(C.byref(c), 1 << 20, 1024, None, C.byref(h)) == B.GPT_EWORKSPACE
+    assert B.lib().gpt_init(C.byref(c), (1 << 20) + 8, 1 << 40, None, C.byref(h)) == B.GPT_EINVAL
+
+
+def test_fp32_path_rejects_head_dim_128():
+    cfg = configs.TINY.replace(n_head=1, head_dim=128)
+    c = B.make_config(cfg)
+    h = C.c_void_p()
+    n = B.gpt_workspace_bytes(cfg)
+    assert B.lib().gpt_init(C.byref(c), 1 << 20, n, None, C.byref(h)) == B.GPT_ESHAPE
+
+
+def test_fwd_bwd_argument_checks_without_gpu():
+    L = B.lib()
+    assert L.gpt_fwd_bwd(None, 1, 1, 1, 1, 1.0, 0, None, None, None, None, None, 1, None) == B.GPT_EINVAL
+
+
+def test_table_entry_point_validation():
+    L = B.lib()
+    # bigram_fwd: bad order, bad dim, bad rows, null pointers
+    assert L.bigram_fwd(16, 2, 4, 4, 100, 16, 1000, 64, B.BF16, 16, None, None) == B.GPT_EINVAL
+    assert L.bigram_fwd(16, 2, 4, 2, 100, 16, 1000, 60, B.BF16, 16, None, None) == B.GPT_ESHAPE
+    assert L.bigram_fwd(16, 2, 4, 2, 100, 16, 0, 64, B.BF16, 16, None, None) == B.GPT_ERANGE
+    assert L.bigram_fwd(None, 2, 4, 2, 100, 16, 1000, 64, B.BF16, 16, None, None) == B.GPT_EINVAL
+    assert L.bigram_fwd(None, 0, 4, 2, 100, None, 1000, 64, B.BF16, None, None, None) == B.GPT_OK
+    # bigram_bwd_update: n = 0 is a no-op; too little workspace is refused
+    assert L.bigram_bwd_update(None, None, 0, 64, B.BF16, None, None, 10, 0.1, 0.95, 1e-8, None, 0, None) == B.GPT_OK
+    need = L.bigram_workspace_bytes(1000, 64, 1 << 20)
+    assert need > 1000 * 16
+    assert L.bigram_bwd_update(16, 16, 1000, 64, B.BF16, 16, 16, 1 << 20, 0.1, 0.95, 1e-8, 256,
+                               need - 1, None) == B.GPT_EWORKSPACE
+    assert L.bigram_bwd_update(16, 16, 1000, 4096, B.BF16, 16, 16, 1 << 20, 0.1, 0.95, 1e-8, 256,
+                               need, None) == B.GPT_ESHAPE
+
+
+def test_status_strings():
+    for s in (B.GPT_OK, B.GPT_EINVAL, B.GPT_ESHAPE, B.GPT_ERANGE, B.GPT_EWORKSPACE, B.GPT_EHIP):
+        assert B.lib().gpt_status_string(s).decode() not in ("", "unknown status")

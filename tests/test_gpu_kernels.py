@@ -1,0 +1,213 @@
+"""GPU parity of each stage of the step (GEMM layouts, RMSNorm, rotary + QK-norm, attention,
+softcapped cross-entropy) against the oracle's primitives, through the per-kernel C ABI."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpt_lm_step_amd import binding as B
+from gpt_lm_step_amd import inputs
+from oracle import model as om
+
+from gpu_util import dev, host, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+BF, F32 = torch.bfloat16, torch.float32
+
+
+def _operand(rng_seed, rows, K, kc, dtype):
+    """Random (rows x K) logical operand and its device storage in the requested layout."""
+    a = inputs.normal(rng_seed, (rows, K), 1.0, dtype == BF)
+    stored = a if kc else np.ascontiguousarray(a.T)
+    return a, dev(stored, dtype)
+
+
+@pytest.mark.parametrize("dtype", [BF, F32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("a_kc,b_kc", [(1, 1), (1, 0), (0, 0), (0, 1)])
+@pytest.mark.parametrize("M,N,K", [(256, 384, 128), (200, 136, 72), (8, 8, 8), (392, 520, 1032)])
+def test_gemm_layouts(dtype, a_kc, b_kc, M, N, K):
+    a, ta = _operand(1, M, K, a_kc, dtype)
+    b, tb = _operand(2, N, K, b_kc, dtype)
+    lda = K if a_kc else M
+    ldb = K if b_kc else N
+    c = torch.full((M, N), float("nan"), device="cuda")
+    B.gptk_gemm(a_kc, b_kc, M, N, K, ta, lda, tb, ldb, c, N, beta=0)
+    want = a.astype(np.float64) @ b.astype(np.float64).T
+    tol = 1e-5
+    assert rel_l2(host(c), want) < tol
+    # beta = 1 accumulates
+    B.gptk_gemm(a_kc, b_kc, M, N, K, ta, lda, tb, ldb, c, N, beta=1)
+    assert rel_l2(host(c), 2 * want) < tol
+
+
+def test_gemm_large_square_bf16():
+    M = N = K = 2048
+    a, ta = _operand(3, M, K, 1, BF)
+    b, tb = _operand(4, N, K, 1, BF)
+    c = torch.empty(M, N, device="cuda")
+    B.gptk_gemm(1, 1, M, N, K, ta, K, tb, K, c, N)
+    want = a.astype(np.float64) @ b.astype(np.float64).T
+    assert rel_l2(host(c), want) < 2e-6
+
+
+@pytest.mark.parametrize("dtype", [BF, F32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128, 768, 2048])
+def test_rmsnorm_fwd_bwd(dtype, D):
+    N = 300
+    x = inputs.normal(5, (N, D), 2.0, False)
+    dy = inputs.normal(6, (N, D), 1.0, False)
+    dres = inputs.normal(7, (N, D), 1.0, False)
+    tx = dev(x)
+    y = torch.empty(N, D, device="cuda", dtype=dtype)
+    r = torch.empty(N, device="cuda")
+    B.gptk_rmsnorm_fwd(tx, y, r, 1e-6)
+    y_want, r_want = om.rms_norm(x.astype(np.float64), 1e-6)
+    np.testing.assert_allclose(host(r), r_want, rtol=2e-6)
+    assert rel_l2(host(y), y_want) < (3e-3 if dtype == BF else 1e-6)
+    dx = dev(dres)
+    dx_t = torch.empty(N, D, device="cuda", dtype=dtype)
+    B.gptk_rmsnorm_bwd(tx, dev(r_want.astype(np.float32)), dev(dy), dx, dx, dx_t)
+    want = dres + om.rms_norm_bwd(y_want, r_want, dy.astype(np.float64))
+    assert rel_l2(host(dx), want) < 1e-6
+    assert rel_l2(host(dx_t), want) < (3e-3 if dtype == BF else 1e-6)
+
+
+@pytest.mark.parametrize("dtype,hd", [(BF, 64), (BF, 128), (F32, 32), (BF, 32)])
+def test_rope_qknorm_fwd_bwd(dtype, hd):
+    Bn, T, H = 2, 128, 3
+    D, N = H * hd, 2 * 128
+    bf = dtype == BF
+    qkv0 = inputs.normal(8, (N, 3 * D), 1.0, bf)
+    cos = torch.empty(T, hd // 2, device="cuda", dtype=dtype)
+    sin = torch.empty_like(cos)
+    B.gptk_rope_table(cos, sin, T, hd, 10000.0)
+    c64, s64 = om.rope_tables(T, hd, 10000.0)
+    # the tables the kernels use: fp64 values rounded once to the storage type
+    cq = (inputs.round_bf16(c64.astype(np.float32)) if bf else c64.astype(np.float32))
+    sq = (inputs.round_bf16(s64.astype(np.float32)) if bf else s64.astype(np.float32))
+    assert np.array_equal(host(cos), cq) and np.array_equal(host(sin), sq)
+    cq, sq = cq.astype(np.float64), sq.astype(np.float64)
+    qkv = dev(qkv0, dtype)
+    rstd = torch.empty(N, 2 * H, device="cuda")
+    B.gptk_rope_qknorm_fwd(qkv, cos, sin, rstd, T, H, hd, 1, 1e-6)
+    x = qkv0.astype(np.float64)
+    q = x[:, :D].reshape(Bn, T, H, hd)
+    k = x[:, D:2 * D].reshape(Bn, T, H, hd)
+    qn, rq = om.rms_norm(om.rope(q, cq, sq), 1e-6)
+    kn, rk = om.rms_norm(om.rope(k, cq, sq), 1e-6)
+    got = host(qkv)
+    tol = 4e-3 if bf else 1e-6
+    assert rel_l2(got[:, :D], qn.reshape(N, D)) < tol
+    assert rel_l2(got[:, D:2 * D], kn.reshape(N, D)) < tol
+    assert np.array_equal(got[:, 2 * D:], qkv0[:, 2 * D:])        # v untouched
+    np.testing.assert_allclose(host(rstd)[:, :H], rq.reshape(N, H), rtol=1e-5)
+    np.testing.assert_allclose(host(rstd)[:, H:], rk.reshape(N, H), rtol=1e-5)
+    # backward, fed with the oracle's forward results (saved normalized q/k and their rstd)
+    saved = qkv0.copy()
+    saved[:, :D] = qn.reshape(N, D)
+    saved[:, D:2 * D] = kn.reshape(N, D)
+    if bf:
+        saved = inputs.round_bf16(saved.astype(np.float32))
+    r = np.concatenate([rq.reshape(N, H), rk.reshape(N, H)], 1).astype(np.float32)
+    dq = inputs.normal(9, (N, 3 * D), 1.0, bf)
+    tdq = dev(dq, dtype)
+    B.gptk_rope_qknorm_bwd(tdq, dev(saved, dtype), cos, sin, dev(r), T, H, hd, 1)
+    y = saved.astype(np.float64)
+    for blk in (0, 1):
+        yy = y[:, blk * D:(blk + 1) * D].reshape(Bn, T, H, hd)
+        rr = r[:, blk * H:(blk + 1) * H].astype(np.float64).reshape(Bn, T, H)
+        dd = dq[:, blk * D:(blk + 1) * D].astype(np.float64).reshape(Bn, T, H, hd)
+        want = om.rope_bwd(om.rms_norm_bwd(yy, rr, dd), cq, sq).reshape(N, D)
+        assert rel_l2(host(tdq)[:, blk * D:(blk + 1) * D], want) < tol
+
+
+def _attn_case(dtype, Bn, T, H, hd, seed):
+    D = H * hd
+    bf = dtype == BF
+    qkv = inputs.normal(seed, (Bn * T, 3 * D), 1.0, bf)
+    # QK-normed q and k have unit RMS; scale like that so softmax is not saturated
+    return qkv
+
+
+def _heads(x, Bn, T, H, hd, blk):
+    D = H * hd
+    return x[:, blk * D:(blk + 1) * D].reshape(Bn, T, H, hd).transpose(0, 2, 1, 3)
+
+
+@pytest.mark.parametrize("dtype,hd,T", [(BF, 64, 256), (BF, 128, 192), (BF, 32, 64),
+                                        (F32, 32, 128), (F32, 64, 64)])
+def test_attention_fwd_bwd(dtype, hd, T):
+    Bn, H = 2, 3
+    D, N = H * hd, Bn * T
+    bf = dtype == BF
+    qkv0 = _attn_case(dtype, Bn, T, H, hd, 10)
+    tq = dev(qkv0, dtype)
+    out = torch.empty(N, D, device="cuda", dtype=dtype)
+    lse2 = torch.empty(Bn, H, T, device="cuda")
+    B.gptk_attention_fwd(tq, out, lse2, Bn, T, H, hd)
+    x = qkv0.astype(np.float64)
+    q, k, v = (_heads(x, Bn, T, H, hd, i) for i in range(3))
+    o, p = om.causal_attention(q, k, v)
+    o_tok = o.transpose(0, 2, 1, 3).reshape(N, D)
+    tol = 1e-2 if bf else 1e-5
+    assert rel_l2(host(out), o_tok) < tol
+    s = (q @ k.transpose(0, 1, 3, 2)) / math.sqrt(hd)
+    s = np.where(np.triu(np.ones((T, T), bool), 1), -np.inf, s)
+    m = s.max(-1)
+    lse = m + np.log(np.exp(s - m[..., None]).sum(-1))
+    np.testing.assert_allclose(host(lse2) * math.log(2), lse, rtol=0, atol=(2e-3 if bf else 1e-5))
+    # backward, fed with the oracle's forward results (O rounded to the storage type, LSE)
+    do = inputs.normal(11, (N, D), 1.0, bf)
+    o_in = inputs.round_bf16(o_tok.astype(np.float32)) if bf else o_tok.astype(np.float32)
+    dqkv = torch.full((N, 3 * D), float("nan"), device="cuda", dtype=dtype)
+    scratch = torch.empty(Bn * H * T, device="cuda")
+    B.gptk_attention_bwd(tq, dev(o_in, dtype), dev(do, dtype),
+                         dev((lse / math.log(2)).astype(np.float32)), scratch, dqkv, Bn, T, H, hd)
+    o_h = o_in.astype(np.float64).reshape(Bn, T, H, hd).transpose(0, 2, 1, 3)
+    do_h = do.astype(np.float64).reshape(Bn, T, H, hd).transpose(0, 2, 1, 3)
+    dq, dk, dv = om.causal_attention_bwd(q, k, v, p, o_h, do_h)
+    got = host(dqkv)
+    for i, want in enumerate((dq, dk, dv)):
+        w = want.transpose(0, 2, 1, 3).reshape(N, D)
+        assert rel_l2(got[:, i * D:(i + 1) * D], w) < (2e-2 if bf else 1e-5), i
+
+
+def test_attention_single_key_rows_and_constant_keys():
+    """The first position attends only to itself (o_0 = v_0), and with identical keys
+    o_t = mean_{s<=t} v_s (closed forms that hold at any size)."""
+    Bn, T, H, hd = 1, 128, 2, 64
+    D, N = H * hd, T
+    qkv0 = inputs.normal(12, (N, 3 * D), 1.0, False)
+    qkv0[:, D:2 * D] = qkv0[0, D:2 * D]                      # constant keys
+    out = torch.empty(N, D, device="cuda")
+    lse2 = torch.empty(Bn, H, T, device="cuda")
+    B.gptk_attention_fwd(dev(qkv0), out, lse2, Bn, T, H, hd)
+    v = qkv0[:, 2 * D:].astype(np.float64)
+    want = np.cumsum(v, 0) / np.arange(1, T + 1)[:, None]
+    np.testing.assert_allclose(host(out), want, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("dtype,V", [(BF, 50304), (BF, 65536), (F32, 512), (BF, 512)])
+def test_softcap_cross_entropy(dtype, V):
+    rows = 37
+    bf = dtype == BF
+    z0 = inputs.normal(13, (rows, V), 3.0, bf)
+    z0[0, :] = 0.0                                    # uniform row: loss = ln V
+    z0[1, 5] = 400.0                                  # saturated softcap
+    tgt = np.random.default_rng(14).integers(0, V, rows).astype(np.int32)
+    tgt[2] = -1
+    tgt[3] = V - 1
+    nv = int(np.sum(tgt >= 0))
+    tz = dev(z0, dtype)
+    loss = torch.empty(rows, device="cuda")
+    B.gptk_softcap_ce(tz, dev(tgt), torch.tensor([nv], dtype=torch.int32, device="cuda"), loss,
+                      cap=15.0, grad_scale=0.5)
+    l_want, g_want = om.softcap_cross_entropy(z0.astype(np.float64), tgt.astype(np.int64), 15.0)
+    np.testing.assert_allclose(host(loss), l_want, rtol=(1e-5 if not bf else 2e-5), atol=1e-5)
+    assert host(loss)[0] == pytest.approx(math.log(V), rel=1e-5)
+    assert host(loss)[2] == 0.0
+    g = host(tz)
+    assert rel_l2(g, g_want * 0.5 / nv) < (5e-3 if bf else 1e-5)
+    assert np.all(g[2] == 0)

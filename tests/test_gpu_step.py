@@ -1,0 +1,215 @@
+"""GPU parity of the whole training step (gpt_fwd_bwd) against the oracle.
+
+Tolerances: fp32 path loss rel err <= 1e-5 and per-tensor gradient rel-L2 <= 1e-4; bf16 path
+loss rel err <= 1e-2, per-tensor gradient rel-L2 <= 3e-2 and cosine >= 0.999.
+
+At full launch sizes the oracle cannot run the whole batch, so only a sample of sequences
+carries targets (the rest are -1): sequences are independent and ignored targets contribute
+nothing, so the step's loss and every gradient equal the oracle's on those sequences alone.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpt_lm_step_amd import binding as B
+from gpt_lm_step_amd import configs, inputs
+from oracle import model as om
+from oracle import tables as ot
+
+from gpu_util import cosine, dev, host, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+class Step:
+    """Device buffers + context for one config."""
+
+    def __init__(self, cfg, params):
+        self.cfg = cfg
+        self.dtype = torch.bfloat16 if cfg.dtype == configs.BF16 else torch.float32
+        self.ctx = B.gpt_init(cfg)
+        self.params = dev(inputs.flatten_params(cfg, params), self.dtype)
+        self.grads = torch.full((configs.param_elems(cfg),), float("nan"), device="cuda")
+        self.loss = torch.zeros(1, device="cuda")
+        N, D = cfg.tokens, cfg.d_model
+        self.d_x0 = torch.full((N, D), float("nan"), device="cuda", dtype=self.dtype)
+        self.d_v = torch.full((N, D), float("nan"), device="cuda", dtype=self.dtype)
+
+    def run(self, tokens, targets, x0=None, va=None, tri=None, grad_scale=1.0, accumulate=0):
+        c = self.cfg
+        T = c.seq_len
+        t_in = dev(np.ascontiguousarray(tokens[:, :T]).astype(np.int32))
+        t_tg = dev(np.ascontiguousarray(targets).astype(np.int32))
+        add = lambda a: None if a is None else dev(a, self.dtype)
+        B.gpt_fwd_bwd(self.ctx, t_in, t_tg, self.params, self.grads, self.loss, grad_scale,
+                      accumulate, add(x0), add(va), add(tri),
+                      self.d_x0 if c.has_x0_add else None,
+                      self.d_v if (c.has_v_add or c.has_trigram) else None)
+        torch.cuda.synchronize()
+        return float(self.loss.item())
+
+    def grad_dict(self):
+        return inputs.unflatten(self.cfg, host(self.grads))
+
+
+def _compare(cfg, res, step, loss, tol_loss, tol_g, cos_min=None, extra=()):
+    assert abs(loss - res.loss) <= tol_loss * abs(res.loss), (loss, res.loss)
+    got = step.grad_dict()
+    worst = {}
+    for name, want in res.grads.items():
+        e = rel_l2(got[name], want)
+        worst[name] = e
+        assert e <= tol_g, (name, e)
+        if cos_min is not None:
+            assert cosine(got[name], want) >= cos_min, name
+    for name, g, want in extra:
+        e = rel_l2(g, want)
+        assert e <= tol_g, (name, e)
+        if cos_min is not None:
+            assert cosine(g, want) >= cos_min, name
+    return worst
+
+
+def _tiny(tables, trigram, seed=101):
+    cfg = configs.TINY.replace(has_x0_add=int(tables), has_v_add=int(tables),
+                               has_trigram=int(trigram))
+    params = inputs.model_params(cfg, seed)
+    tok = inputs.uniform_tokens(1, (cfg.batch, cfg.seq_len + 1), cfg.vocab)
+    N, D = cfg.tokens, cfg.d_model
+    x0 = inputs.addend(11, N, D, 0.02, False) if tables else None
+    va = inputs.addend(12, N, D, 0.02, False) if tables else None
+    tri = inputs.addend(13, N, D, 1.0, False) if trigram else None
+    return cfg, params, tok, x0, va, tri
+
+
+@pytest.mark.parametrize("tables,trigram", [(False, False), (True, False), (True, True)])
+def test_tiny_fp32_step_matches_oracle(tables, trigram):
+    cfg, params, tok, x0, va, tri = _tiny(tables, trigram)
+    step = Step(cfg, params)
+    loss = step.run(tok, tok[:, 1:], x0, va, tri)
+    res = om.forward_backward(cfg, params, tok, x0, va, tri)
+    extra = []
+    if tables:
+        extra.append(("d_x0_add", host(step.d_x0), res.d_x0_add))
+        extra.append(("d_v_add", host(step.d_v), res.d_v_add))
+    _compare(cfg, res, step, loss, 1e-5, 1e-4, extra=extra)
+
+
+def test_tiny_fp32_ignored_targets_scale_and_accumulation():
+    cfg, params, tok, _, _, _ = _tiny(False, False)
+    tgt = tok[:, 1:].copy()
+    tgt[np.random.default_rng(3).random(tgt.shape) < 0.1] = -1
+    step = Step(cfg, params)
+    loss = step.run(tok, tgt, grad_scale=0.25)
+    res = om.forward_backward(cfg, params, tok, targets=tgt, grad_scale=0.25)
+    _compare(cfg, res, step, loss, 1e-5, 1e-4)
+    # accumulate a second micro-batch with other tokens
+    tok2 = inputs.uniform_tokens(2, tok.shape, cfg.vocab)
+    step.run(tok2, tok2[:, 1:], grad_scale=0.25, accumulate=1)
+    res2 = om.forward_backward(cfg, params, tok2, grad_scale=0.25)
+    got = step.grad_dict()
+    for name in res.grads:
+        assert rel_l2(got[name], res.grads[name] + res2.grads[name]) <= 1e-4, name
+
+
+def test_tiny_zero_head_loss_is_ln_vocab_and_other_grads_vanish():
+    cfg = configs.TINY
+    params = inputs.model_params(cfg, 101, zero_head=True)
+    tok = inputs.uniform_tokens(1, (cfg.batch, cfg.seq_len + 1), cfg.vocab)
+    step = Step(cfg, params)
+    loss = step.run(tok, tok[:, 1:])
+    assert loss == pytest.approx(math.log(cfg.vocab), rel=1e-6)
+    g = step.grad_dict()
+    for name, v in g.items():
+        if name != "lm_head":
+            assert np.all(v == 0.0), name
+
+
+def test_step_is_bitwise_deterministic():
+    cfg, params, tok, x0, va, tri = _tiny(True, True)
+    step = Step(cfg, params)
+    step.run(tok, tok[:, 1:], x0, va, tri)
+    g1, d1 = step.grads.clone(), step.d_v.clone()
+    step.run(tok, tok[:, 1:], x0, va, tri)
+    assert torch.equal(g1, step.grads) and torch.equal(d1, step.d_v)
+
+
+def test_out_of_range_ids_are_flagged_not_faulting():
+    cfg, params, tok, _, _, _ = _tiny(False, False)
+    step = Step(cfg, params)
+    bad = tok.copy()
+    bad[0, 3] = cfg.vocab + 7
+    bad[1, 5] = -4
+    tgt = bad[:, 1:].copy()
+    tgt[2, 2] = cfg.vocab
+    loss = step.run(bad, tgt)
+    assert math.isfinite(loss)
+    assert B.gpt_check_errors(step.ctx) == 3
+    assert B.gpt_check_errors(step.ctx) == 0
+
+
+def _sampled_targets(tok, T, keep):
+    tgt = np.full((tok.shape[0], T), -1, np.int32)
+    for b in keep:
+        tgt[b] = tok[b, 1:]
+    return tgt
+
+
+def test_gpt2_small_bf16_full_launch_sampled_sequences():
+    """GPT-2-small shape at its full launch size (B=8, T=1024, V=50304), Zipf tokens; sequences
+    0 and 5 carry targets and are recomputed by the oracle."""
+    cfg = configs.GPT2_SMALL
+    params = inputs.model_params(cfg, 102)
+    tok = inputs.step_tokens(cfg, 2)
+    keep = [0, 5]
+    step = Step(cfg, params)
+    loss = step.run(tok, _sampled_targets(tok, cfg.seq_len, keep))
+    sub = cfg.replace(batch=len(keep))
+    res = om.forward_backward(sub, params, tok[keep])
+    _compare(cfg, res, step, loss, 1e-2, 3e-2, cos_min=0.999)
+
+
+def test_speedrun_microbatch_with_tables_sampled():
+    """Speedrun shape: GPT-2-small model + x0 bigram (2^21 rows), value bigram (2^20 rows) and
+    the frozen trigram table (2^21 rows, N(0,1)) projected by wtri, one 8 x 1024 micro-batch;
+    the addends come from bigram_fwd, the oracle rebuilds them from the same tables."""
+    cfg = configs.SPEEDRUN
+    tc = configs.TABLES
+    params = inputs.model_params(cfg, 102)
+    tok = inputs.step_tokens(cfg, 5)
+    keep = [3]
+    T, N, D = cfg.seq_len, cfg.tokens, cfg.d_model
+    g = torch.Generator(device="cuda").manual_seed(104)
+    tx0 = (torch.randn(tc.x0_rows, D, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    tv = (torch.randn(tc.v_rows, D, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    ttri = torch.randn(tc.tri_rows, D, device="cuda", generator=g).to(torch.bfloat16)
+    t_in = dev(np.ascontiguousarray(tok[:, :T]).astype(np.int32))
+    adds = []
+    for table, order in ((tx0, 2), (tv, 2), (ttri, 3)):
+        y = torch.zeros(N, D, device="cuda", dtype=torch.bfloat16)
+        B.bigram_fwd(t_in, order, cfg.vocab, table, y)
+        adds.append(y)
+    step = Step(cfg, params)
+    c = cfg
+    B.gpt_fwd_bwd(step.ctx, t_in, dev(_sampled_targets(tok, T, keep)), step.params, step.grads,
+                  step.loss, 1.0, 0, adds[0], adds[1], adds[2], step.d_x0, step.d_v)
+    torch.cuda.synchronize()
+    loss = float(step.loss.item())
+    # oracle addends for the kept sequence, from the same tables
+    sel = tok[keep, :T]
+    rows = []
+    for table, order, R in ((tx0, 2, tc.x0_rows), (tv, 2, tc.v_rows), (ttri, 3, tc.tri_rows)):
+        h = ot.hash_indices(sel, order, cfg.vocab, R).reshape(-1)
+        rows.append(host(table[torch.from_numpy(h).cuda()]))
+    sub = cfg.replace(batch=len(keep))
+    res = om.forward_backward(sub, params, tok[keep], rows[0], rows[1], rows[2])
+    tsl = slice(keep[0] * T, (keep[0] + 1) * T)
+    extra = [("d_x0_add", host(step.d_x0)[tsl], res.d_x0_add),
+             ("d_v_add", host(step.d_v)[tsl], res.d_v_add)]
+    _compare(cfg, res, step, loss, 1e-2, 3e-2, cos_min=0.999, extra=extra)
+    # tokens of the other sequences get exactly zero addend gradients
+    other = np.ones(N, bool)
+    other[tsl] = False
+    assert np.all(host(step.d_x0)[other] == 0) and np.all(host(step.d_v)[other] == 0)
