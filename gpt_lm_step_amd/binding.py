@@ -21,7 +21,7 @@ F32, BF16 = 0, 1
 # Every symbol include/gpt.h declares.
 EXPORTS = [
     "gpt_param_layout", "gpt_workspace_bytes", "gpt_init", "gpt_fwd_bwd", "gpt_check_errors",
-    "gpt_destroy", "bigram_fwd", "bigram_workspace_bytes", "bigram_bwd_update",
+    "gpt_profile", "gpt_profile_read", "gpt_destroy", "bigram_fwd", "bigram_workspace_bytes", "bigram_bwd_update",
     "gpt_last_error", "gpt_status_string",
 ]
 # Every symbol include/gpt_kernels.h declares.
@@ -45,6 +45,11 @@ class gpt_config(C.Structure):
                [(n, C.c_int32) for n in ("qk_norm", "has_x0_add", "has_v_add", "has_trigram")]
 
 
+class gpt_profile_entry(C.Structure):
+    _fields_ = [("name", C.c_char * 32), ("calls", C.c_int32), ("ms", C.c_float),
+                ("flops", C.c_double), ("bytes", C.c_double)]
+
+
 class gpt_tensor_desc(C.Structure):
     _fields_ = [("name", C.c_char * 48), ("offset_elems", C.c_int64), ("ndim", C.c_int32),
                 ("shape", C.c_int64 * 2)]
@@ -66,6 +71,8 @@ def lib() -> C.CDLL:
             "gpt_fwd_bwd": (i32, [vp, vp, vp, vp, vp, f32, i32, vp, vp, vp, vp, vp, vp, vp]),
             "gpt_check_errors": (i32, [vp, vp, C.POINTER(i32)]),
             "gpt_destroy": (i32, [vp]),
+            "gpt_profile": (i32, [vp, i32]),
+            "gpt_profile_read": (i32, [vp, vp, C.POINTER(i32)]),
             "bigram_fwd": (i32, [vp, i32, i32, i32, i32, vp, i64, i32, i32, vp, vp, vp]),
             "bigram_workspace_bytes": (sz, [i64, i32, i64]),
             "bigram_bwd_update": (i32, [vp, vp, i64, i32, i32, vp, vp, i64, f32, f32, f32, vp,
@@ -172,6 +179,20 @@ def gpt_check_errors(ctx: Context, stream=None) -> int:
     f = C.c_int32(0)
     _check(lib().gpt_check_errors(ctx.handle, _stream(stream), C.byref(f)))
     return f.value
+
+
+def gpt_profile(ctx: Context, enable: bool):
+    _check(lib().gpt_profile(ctx.handle, int(bool(enable))))
+
+
+def gpt_profile_read(ctx: Context):
+    """[(name, calls, ms, flops, bytes)] aggregated per stage since profiling was enabled."""
+    n = C.c_int32(0)
+    arr = (gpt_profile_entry * 256)()
+    n.value = 256
+    _check(lib().gpt_profile_read(ctx.handle, arr, C.byref(n)))
+    return [(arr[i].name.decode(), arr[i].calls, arr[i].ms, arr[i].flops, arr[i].bytes)
+            for i in range(min(n.value, 256))]
 
 
 def gpt_destroy(ctx: Context):

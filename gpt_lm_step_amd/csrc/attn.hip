@@ -429,21 +429,36 @@ gpt_status launch_attn_fwd(const T* qkv, T* out, float* lse2, int B, int Tn, int
 }
 
 template <typename T>
-gpt_status launch_attn_bwd(const T* qkv, const T* out, const T* dout, const float* lse2,
-                           float* dq_sum, T* dqkv, int B, int Tn, int H, int hd, hipStream_t s) {
+gpt_status launch_attn_bwd_stage(int stage, const T* qkv, const T* out, const T* dout,
+                                 const float* lse2, float* dq_sum, T* dqkv, int B, int Tn, int H,
+                                 int hd, hipStream_t s) {
   const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
   const float scale = 1.f / sqrtf((float)hd);
   const long long N = (long long)B * Tn;
   dim3 grid(cdiv(Tn, 128), H, B);
   gpt_status st = dispatch_hd<T>(hd, [&](auto HD) {
     constexpr int hdv = decltype(HD)::value;
-    attn_bwd_pre_kernel<T, hdv><<<cdiv(N * H, 256), 256, 0, s>>>(out, dout, dq_sum, N, Tn, H);
-    attn_bwd_dkdv_kernel<T, hdv><<<grid, ATHREADS, 0, s>>>(qkv, dout, lse2, dq_sum, dqkv, Tn, H,
+    if (stage == 0)
+      attn_bwd_pre_kernel<T, hdv><<<cdiv(N * H, 256), 256, 0, s>>>(out, dout, dq_sum, N, Tn, H);
+    else if (stage == 1)
+      attn_bwd_dkdv_kernel<T, hdv><<<grid, ATHREADS, 0, s>>>(qkv, dout, lse2, dq_sum, dqkv, Tn, H,
+                                                             sl2, scale);
+    else
+      attn_bwd_dq_kernel<T, hdv><<<grid, ATHREADS, 0, s>>>(qkv, dout, lse2, dq_sum, dqkv, Tn, H,
                                                            sl2, scale);
-    attn_bwd_dq_kernel<T, hdv><<<grid, ATHREADS, 0, s>>>(qkv, dout, lse2, dq_sum, dqkv, Tn, H,
-                                                         sl2, scale);
   });
   return st != GPT_OK ? st : check_launch("attention bwd");
+}
+
+template <typename T>
+gpt_status launch_attn_bwd(const T* qkv, const T* out, const T* dout, const float* lse2,
+                           float* dq_sum, T* dqkv, int B, int Tn, int H, int hd, hipStream_t s) {
+  for (int stage = 0; stage < 3; ++stage) {
+    gpt_status st = launch_attn_bwd_stage<T>(stage, qkv, out, dout, lse2, dq_sum, dqkv, B, Tn, H,
+                                             hd, s);
+    if (st != GPT_OK) return st;
+  }
+  return GPT_OK;
 }
 
 template gpt_status launch_attn_fwd<float>(const float*, float*, float*, int, int, int, int,
@@ -454,5 +469,11 @@ template gpt_status launch_attn_bwd<float>(const float*, const float*, const flo
                                            float*, float*, int, int, int, int, hipStream_t);
 template gpt_status launch_attn_bwd<bf16>(const bf16*, const bf16*, const bf16*, const float*,
                                           float*, bf16*, int, int, int, int, hipStream_t);
+template gpt_status launch_attn_bwd_stage<float>(int, const float*, const float*, const float*,
+                                                 const float*, float*, float*, int, int, int, int,
+                                                 hipStream_t);
+template gpt_status launch_attn_bwd_stage<bf16>(int, const bf16*, const bf16*, const bf16*,
+                                                const float*, float*, bf16*, int, int, int, int,
+                                                hipStream_t);
 
 }  // namespace gpt

@@ -18,8 +18,8 @@ gpt_status gptk_gemm(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32
   if (M < 0 || N < 0 || K < 0 || ldc < N) return fail(GPT_ESHAPE, "gptk_gemm: bad sizes");
   EpiStoreF32 epi{C, ldc, beta ? 1 : 0};
   if (dtype == GPT_BF16)
-    return gemm<bf16>(a_kc, b_kc, M, N, K, (const bf16*)A, lda, (const bf16*)B, ldb, epi, stream);
-  return gemm<float>(a_kc, b_kc, M, N, K, (const float*)A, lda, (const float*)B, ldb, epi, stream);
+    return gemm<G_TEST, bf16>(a_kc, b_kc, M, N, K, (const bf16*)A, lda, (const bf16*)B, ldb, epi, stream);
+  return gemm<G_TEST, float>(a_kc, b_kc, M, N, K, (const float*)A, lda, (const float*)B, ldb, epi, stream);
 }
 
 gpt_status gptk_rmsnorm_fwd(int32_t dtype, const float* x, void* y, float* rstd, int64_t N,

@@ -152,6 +152,31 @@ Plan carve_plan(const gpt_config& c, Carver& cv) {
   return p;
 }
 
+// Optional per-launch timing: when enabled, every launch of a step is bracketed by two events
+// on the step's stream and tagged with its stage name and algorithmic work.
+struct ProfRec {
+  const char* name;
+  double flops, bytes;
+  hipEvent_t a, b;
+};
+struct Prof {
+  bool on = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  size_t next = 0;
+  hipEvent_t get() {
+    if (next == pool.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[next++];
+  }
+  ~Prof() {
+    for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+  }
+};
+
 }  // namespace
 }  // namespace gpt
 
@@ -161,6 +186,7 @@ struct gpt_ctx {
   gpt::Plan plan;
   void* ws;
   size_t ws_bytes;
+  gpt::Prof prof;
 };
 
 namespace gpt {
@@ -173,33 +199,52 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
   const gpt_config& c = ctx->cfg;
   const Layout& Ly = ctx->layout;
   Plan& p = ctx->plan;
+  Prof& prof = ctx->prof;
   const long long N = (long long)c.batch * c.seq_len;
   const int D = c.d_model, F = c.d_mlp, V = c.vocab, H = c.n_head, hd = c.head_dim;
   const int Lc = c.n_layer, Tn = c.seq_len, Bn = c.batch;
   const int beta = accumulate ? 1 : 0;
   const bool vadd = c.has_v_add || c.has_trigram;
   const float eps = c.rms_eps;
+  const double es = sizeof(T);
+  const double ND = (double)N * D;
+  const double pairs = (double)Bn * H * Tn * (Tn + 1) / 2.0;  // causal (query, key) pairs
   const T* cos_t = (const T*)p.cos_t;
   const T* sin_t = (const T*)p.sin_t;
+  // Run one stage; with profiling on, bracket it by events and record its algorithmic work.
+  auto run = [&](const char* name, double flops, double bytes, auto&& fn) -> gpt_status {
+    if (!prof.on) return fn();
+    hipEvent_t e0 = prof.get(), e1 = prof.get();
+    if (!e0 || !e1) return fail(GPT_EHIP, "profiling: hipEventCreate failed");
+    (void)hipEventRecord(e0, s);
+    gpt_status st = fn();
+    (void)hipEventRecord(e1, s);
+    prof.recs.push_back({name, flops, bytes, e0, e1});
+    return st;
+  };
+  auto mm = [](double m, double n, double k) { return 2.0 * m * n * k; };
 #define TRY(x)                          \
   do {                                  \
     gpt_status st_ = (x);               \
     if (st_ != GPT_OK) return st_;      \
   } while (0)
+#define STAGE(name, flops, bytes, ...) TRY(run(name, flops, bytes, [&]() { return __VA_ARGS__; }))
 
   // value addend u = v_add + tri_rows wtri^T (fp32), shared by every layer
   const float* u = nullptr;
   if (c.has_trigram) {
-    TRY(gemm<T>(true, true, (int)N, D, D, tri_rows, D, P + Ly.wtri, D,
-                EpiAddRows<T>{c.has_v_add ? v_add : nullptr, p.u, D}, s));
+    STAGE("tri_proj", mm(N, D, D), 0,
+          gemm<G_TRI, T>(true, true, (int)N, D, D, tri_rows, D, P + Ly.wtri, D,
+                         EpiAddRows<T>{c.has_v_add ? v_add : nullptr, p.u, D}, s));
     u = p.u;
   } else if (c.has_v_add) {
-    TRY(launch_accum_rows<T>(p.u, v_add, D, N, D, 0, s));
+    STAGE("vadd_cast", 0, ND * (es + 4), launch_accum_rows<T>(p.u, v_add, D, N, D, 0, s));
     u = p.u;
   }
-  TRY(launch_count_targets(targets, N, V, p.n_valid, p.err, s));
-  TRY(launch_embed_fwd<T>(tokens, P + Ly.wte, c.has_x0_add ? x0_add : nullptr, p.L[0].x_in,
-                          p.e_rstd, p.tok_c, p.err, N, D, V, eps, s));
+  STAGE("count_targets", 0, 4.0 * N, launch_count_targets(targets, N, V, p.n_valid, p.err, s));
+  STAGE("embed_fwd", 0, ND * (es + (c.has_x0_add ? es : 0) + 4) + 12.0 * N,
+        launch_embed_fwd<T>(tokens, P + Ly.wte, c.has_x0_add ? x0_add : nullptr, p.L[0].x_in,
+                            p.e_rstd, p.tok_c, p.err, N, D, V, eps, s));
 
   // ---------------- forward
   for (int l = 0; l < Lc; ++l) {
@@ -207,34 +252,51 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
     T *a = (T*)b.a, *qkv = (T*)b.qkv, *o = (T*)b.o, *bb = (T*)b.b, *hp = (T*)b.hp,
       *act = (T*)b.act;
     float* x_out = l + 1 < Lc ? p.L[l + 1].x_in : p.x_final;
-    TRY(launch_rms_fwd<T>(b.x_in, a, b.rstd_a, N, D, eps, s));
-    TRY(gemm<T>(true, true, (int)N, 3 * D, D, a, D, P + Ly.wqkv[l], D,
-                EpiQKV<T>{qkv, 3LL * D, u, D, 2 * D}, s));
-    TRY(launch_rope_qknorm_fwd<T>(qkv, cos_t, sin_t, b.rstd_qk, N, Tn, H, hd, c.qk_norm, eps, s));
-    TRY(launch_attn_fwd<T>(qkv, o, b.lse, Bn, Tn, H, hd, s));
-    TRY(gemm<T>(true, true, (int)N, D, D, o, D, P + Ly.wo[l], D, EpiResid{b.x_in, b.x_mid, D}, s));
-    TRY(launch_rms_fwd<T>(b.x_mid, bb, b.rstd_b, N, D, eps, s));
-    TRY(gemm<T>(true, true, (int)N, F, D, bb, D, P + Ly.wfc[l], D, EpiRelu2<T>{hp, act, F}, s));
-    TRY(gemm<T>(true, true, (int)N, D, F, act, F, P + Ly.wpr[l], F, EpiResid{b.x_mid, x_out, D}, s));
+    STAGE("rmsnorm_fwd", 0, ND * (4 + es) + 4.0 * N,
+          launch_rms_fwd<T>(b.x_in, a, b.rstd_a, N, D, eps, s));
+    STAGE("qkv_fwd", mm(N, 3 * D, D), 0,
+          gemm<G_QKV, T>(true, true, (int)N, 3 * D, D, a, D, P + Ly.wqkv[l], D,
+                         EpiQKV<T>{qkv, 3LL * D, u, D, 2 * D}, s));
+    STAGE("rope_qknorm_fwd", 0, 4.0 * ND * es + 8.0 * N * H,
+          launch_rope_qknorm_fwd<T>(qkv, cos_t, sin_t, b.rstd_qk, N, Tn, H, hd, c.qk_norm, eps, s));
+    STAGE("attn_fwd", 4.0 * pairs * hd, 0, launch_attn_fwd<T>(qkv, o, b.lse, Bn, Tn, H, hd, s));
+    STAGE("out_fwd", mm(N, D, D), 0,
+          gemm<G_OUT, T>(true, true, (int)N, D, D, o, D, P + Ly.wo[l], D,
+                         EpiResid{b.x_in, b.x_mid, D}, s));
+    STAGE("rmsnorm_fwd", 0, ND * (4 + es) + 4.0 * N,
+          launch_rms_fwd<T>(b.x_mid, bb, b.rstd_b, N, D, eps, s));
+    STAGE("up_fwd", mm(N, F, D), 0,
+          gemm<G_UP, T>(true, true, (int)N, F, D, bb, D, P + Ly.wfc[l], D,
+                        EpiRelu2<T>{hp, act, F}, s));
+    STAGE("down_fwd", mm(N, D, F), 0,
+          gemm<G_DOWN, T>(true, true, (int)N, D, F, act, F, P + Ly.wpr[l], F,
+                          EpiResid{b.x_mid, x_out, D}, s));
   }
   T* f = (T*)p.f;
-  TRY(launch_rms_fwd<T>(p.x_final, f, p.rstd_f, N, D, eps, s));
+  STAGE("rmsnorm_fwd", 0, ND * (4 + es) + 4.0 * N,
+        launch_rms_fwd<T>(p.x_final, f, p.rstd_f, N, D, eps, s));
 
   // ---------------- LM head + softcapped cross-entropy, chunked over tokens
   T* z = (T*)p.logits;
   const T* wh = P + Ly.lm_head;
   for (long long c0 = 0; c0 < N; c0 += p.ce_rows) {
     const int rows = (int)std::min<long long>(p.ce_rows, N - c0);
-    TRY(gemm<T>(true, true, rows, V, D, f + c0 * D, D, wh, D, EpiStore<T>{z, V}, s));
-    TRY(launch_ce<T>(z, V, targets + c0, rows, V, c.softcap, grad_scale, p.n_valid,
-                     p.loss_rows + c0, s));
-    TRY(gemm<T>(true, false, rows, D, V, z, V, wh, D, EpiStoreF32{p.df + c0 * D, D, 0}, s));
-    TRY(gemm<T>(false, false, V, D, rows, z, V, f + c0 * D, D,
-                EpiStoreF32{G + Ly.lm_head, D, (beta || c0 > 0) ? 1 : 0}, s));
+    STAGE("head_fwd", mm(rows, V, D), 0,
+          gemm<G_HEAD, T>(true, true, rows, V, D, f + c0 * D, D, wh, D, EpiStore<T>{z, V}, s));
+    STAGE("softcap_ce", 0, 2.0 * rows * V * es + 8.0 * rows,
+          launch_ce<T>(z, V, targets + c0, rows, V, c.softcap, grad_scale, p.n_valid,
+                       p.loss_rows + c0, s));
+    STAGE("head_dgrad", mm(rows, D, V), 0,
+          gemm<G_HEAD_DGRAD, T>(true, false, rows, D, V, z, V, wh, D,
+                                EpiStoreF32{p.df + c0 * D, D, 0}, s));
+    STAGE("head_wgrad", mm(V, D, rows), 0,
+          gemm<G_HEAD_WGRAD, T>(false, false, V, D, rows, z, V, f + c0 * D, D,
+                                EpiStoreF32{G + Ly.lm_head, D, (beta || c0 > 0) ? 1 : 0}, s));
   }
-  TRY(launch_loss_reduce(p.loss_rows, N, p.n_valid, loss, s));
+  STAGE("loss_reduce", 0, 4.0 * N, launch_loss_reduce(p.loss_rows, N, p.n_valid, loss, s));
   T* dx_t = (T*)p.dx_t;
-  TRY(launch_rms_bwd<T>(p.x_final, p.rstd_f, p.df, nullptr, p.dx, dx_t, N, D, s));
+  STAGE("rmsnorm_bwd", 0, ND * (12 + es) + 4.0 * N,
+        launch_rms_bwd<T>(p.x_final, p.rstd_f, p.df, nullptr, p.dx, dx_t, N, D, s));
 
   // ---------------- backward through the blocks
   T *dact = (T*)p.dact, *dO = (T*)p.dO, *dqkv = (T*)p.dqkv;
@@ -243,38 +305,69 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
     const T *a = (const T*)b.a, *qkv = (const T*)b.qkv, *o = (const T*)b.o, *bb = (const T*)b.b,
             *hp = (const T*)b.hp, *act = (const T*)b.act;
     // MLP: x_out = x_mid + relu(b Wfc^T)^2 Wpr^T
-    TRY(gemm<T>(true, false, (int)N, F, D, dx_t, D, P + Ly.wpr[l], F, EpiDRelu2<T>{hp, dact, F}, s));
-    TRY(gemm<T>(false, false, D, F, (int)N, dx_t, D, act, F, EpiStoreF32{G + Ly.wpr[l], F, beta}, s));
-    TRY(gemm<T>(true, false, (int)N, D, F, dact, F, P + Ly.wfc[l], D, EpiStoreF32{p.db, D, 0}, s));
-    TRY(gemm<T>(false, false, F, D, (int)N, dact, F, bb, D, EpiStoreF32{G + Ly.wfc[l], D, beta}, s));
-    TRY(launch_rms_bwd<T>(b.x_mid, b.rstd_b, p.db, p.dx, p.dx, dx_t, N, D, s));
+    STAGE("down_dgrad", mm(N, F, D), 0,
+          gemm<G_DOWN_DGRAD, T>(true, false, (int)N, F, D, dx_t, D, P + Ly.wpr[l], F,
+                                EpiDRelu2<T>{hp, dact, F}, s));
+    STAGE("down_wgrad", mm(D, F, N), 0,
+          gemm<G_DOWN_WGRAD, T>(false, false, D, F, (int)N, dx_t, D, act, F,
+                                EpiStoreF32{G + Ly.wpr[l], F, beta}, s));
+    STAGE("up_dgrad", mm(N, D, F), 0,
+          gemm<G_UP_DGRAD, T>(true, false, (int)N, D, F, dact, F, P + Ly.wfc[l], D,
+                              EpiStoreF32{p.db, D, 0}, s));
+    STAGE("up_wgrad", mm(F, D, N), 0,
+          gemm<G_UP_WGRAD, T>(false, false, F, D, (int)N, dact, F, bb, D,
+                              EpiStoreF32{G + Ly.wfc[l], D, beta}, s));
+    STAGE("rmsnorm_bwd", 0, ND * (16 + es) + 4.0 * N,
+          launch_rms_bwd<T>(b.x_mid, b.rstd_b, p.db, p.dx, p.dx, dx_t, N, D, s));
     // attention: x_mid = x_in + O Wo^T
-    TRY(gemm<T>(true, false, (int)N, D, D, dx_t, D, P + Ly.wo[l], D, EpiStore<T>{dO, D}, s));
-    TRY(gemm<T>(false, false, D, D, (int)N, dx_t, D, o, D, EpiStoreF32{G + Ly.wo[l], D, beta}, s));
-    TRY(launch_attn_bwd<T>(qkv, o, dO, b.lse, p.dqsum, dqkv, Bn, Tn, H, hd, s));
-    TRY(launch_rope_qknorm_bwd<T>(dqkv, qkv, cos_t, sin_t, b.rstd_qk, N, Tn, H, hd, c.qk_norm, s));
-    if (vadd) TRY(launch_accum_rows<T>(p.dU, dqkv + 2 * D, 3LL * D, N, D, l != Lc - 1, s));
-    TRY(gemm<T>(true, false, (int)N, D, 3 * D, dqkv, 3 * D, P + Ly.wqkv[l], D,
-                EpiStoreF32{p.db, D, 0}, s));
-    TRY(gemm<T>(false, false, 3 * D, D, (int)N, dqkv, 3 * D, a, D,
-                EpiStoreF32{G + Ly.wqkv[l], D, beta}, s));
-    TRY(launch_rms_bwd<T>(b.x_in, b.rstd_a, p.db, p.dx, p.dx, dx_t, N, D, s));
+    STAGE("out_dgrad", mm(N, D, D), 0,
+          gemm<G_OUT_DGRAD, T>(true, false, (int)N, D, D, dx_t, D, P + Ly.wo[l], D,
+                               EpiStore<T>{dO, D}, s));
+    STAGE("out_wgrad", mm(D, D, N), 0,
+          gemm<G_OUT_WGRAD, T>(false, false, D, D, (int)N, dx_t, D, o, D,
+                               EpiStoreF32{G + Ly.wo[l], D, beta}, s));
+    STAGE("attn_bwd_pre", 0, 2.0 * ND * es + 4.0 * N * H,
+          launch_attn_bwd_stage<T>(0, qkv, o, dO, b.lse, p.dqsum, dqkv, Bn, Tn, H, hd, s));
+    STAGE("attn_bwd_dkdv", 8.0 * pairs * hd, 0,
+          launch_attn_bwd_stage<T>(1, qkv, o, dO, b.lse, p.dqsum, dqkv, Bn, Tn, H, hd, s));
+    STAGE("attn_bwd_dq", 2.0 * pairs * hd, 0,
+          launch_attn_bwd_stage<T>(2, qkv, o, dO, b.lse, p.dqsum, dqkv, Bn, Tn, H, hd, s));
+    STAGE("rope_qknorm_bwd", 0, 6.0 * ND * es + 8.0 * N * H,
+          launch_rope_qknorm_bwd<T>(dqkv, qkv, cos_t, sin_t, b.rstd_qk, N, Tn, H, hd, c.qk_norm, s));
+    if (vadd)
+      STAGE("dvadd_accum", 0, ND * (es + (l != Lc - 1 ? 8 : 4)),
+            launch_accum_rows<T>(p.dU, dqkv + 2 * D, 3LL * D, N, D, l != Lc - 1, s));
+    STAGE("qkv_dgrad", mm(N, D, 3 * D), 0,
+          gemm<G_QKV_DGRAD, T>(true, false, (int)N, D, 3 * D, dqkv, 3 * D, P + Ly.wqkv[l], D,
+                               EpiStoreF32{p.db, D, 0}, s));
+    STAGE("qkv_wgrad", mm(3 * D, D, N), 0,
+          gemm<G_QKV_WGRAD, T>(false, false, 3 * D, D, (int)N, dqkv, 3 * D, a, D,
+                               EpiStoreF32{G + Ly.wqkv[l], D, beta}, s));
+    STAGE("rmsnorm_bwd", 0, ND * (16 + es) + 4.0 * N,
+          launch_rms_bwd<T>(b.x_in, b.rstd_a, p.db, p.dx, p.dx, dx_t, N, D, s));
   }
 
   // ---------------- embedding, x0 addend, value addend
-  if (c.has_x0_add && d_x0_add) TRY(launch_cast<T>(d_x0_add, p.dx, N * D, s));
-  TRY(launch_embed_bwd<T>(p.tok_c, P + Ly.wte, p.e_rstd, p.dx, p.de, N, D, s));
-  if (!accumulate) TRY(launch_fill(G + Ly.wte, (long long)V * D, 0.f, s));
-  TRY(segsum_grad(p.tok_c, p.de, N, D, G + Ly.wte, V, 1, p.seg_ws, p.seg_bytes, s));
+  if (c.has_x0_add && d_x0_add)
+    STAGE("cast", 0, ND * (4 + es), launch_cast<T>(d_x0_add, p.dx, N * D, s));
+  STAGE("embed_bwd", 0, ND * (es + 8) + 8.0 * N,
+        launch_embed_bwd<T>(p.tok_c, P + Ly.wte, p.e_rstd, p.dx, p.de, N, D, s));
+  if (!accumulate)
+    STAGE("fill", 0, 4.0 * V * D, launch_fill(G + Ly.wte, (long long)V * D, 0.f, s));
+  STAGE("wte_segsum", 0, ND * 4 * 2,
+        segsum_grad(p.tok_c, p.de, N, D, G + Ly.wte, V, 1, p.seg_ws, p.seg_bytes, s));
   if (vadd) {
-    if (c.has_v_add && d_v_add) TRY(launch_cast<T>(d_v_add, p.dU, N * D, s));
+    if (c.has_v_add && d_v_add)
+      STAGE("cast", 0, ND * (4 + es), launch_cast<T>(d_v_add, p.dU, N * D, s));
     if (c.has_trigram) {
       T* du_t = (T*)p.du_t;
-      TRY(launch_cast<T>(du_t, p.dU, N * D, s));
-      TRY(gemm<T>(false, false, D, D, (int)N, du_t, D, tri_rows, D,
-                  EpiStoreF32{G + Ly.wtri, D, beta}, s));
+      STAGE("cast", 0, ND * (4 + es), launch_cast<T>(du_t, p.dU, N * D, s));
+      STAGE("tri_wgrad", mm(D, D, N), 0,
+            gemm<G_TRI_WGRAD, T>(false, false, D, D, (int)N, du_t, D, tri_rows, D,
+                                 EpiStoreF32{G + Ly.wtri, D, beta}, s));
     }
   }
+#undef STAGE
 #undef TRY
   return GPT_OK;
 }
@@ -381,6 +474,42 @@ gpt_status gpt_check_errors(gpt_ctx* ctx, hipStream_t stream, int32_t* flags) {
   *flags = h;
   gpt_status st = launch_fill((float*)ctx->plan.err, 1, 0.f, stream);
   return st;
+}
+
+gpt_status gpt_profile(gpt_ctx* ctx, int32_t enable) {
+  if (!ctx) return fail(GPT_EINVAL, "gpt_profile: ctx is null");
+  ctx->prof.on = enable != 0;
+  return GPT_OK;
+}
+
+gpt_status gpt_profile_read(gpt_ctx* ctx, gpt_profile_entry* out, int32_t* count) {
+  if (!ctx || !count) return fail(GPT_EINVAL, "gpt_profile_read: null argument");
+  Prof& pr = ctx->prof;
+  std::vector<gpt_profile_entry> agg;
+  for (const ProfRec& r : pr.recs) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return fail(GPT_EHIP, "gpt_profile_read: event sync failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return fail(GPT_EHIP, "gpt_profile_read: elapsed failed");
+    gpt_profile_entry* e = nullptr;
+    for (auto& x : agg)
+      if (strcmp(x.name, r.name) == 0) e = &x;
+    if (!e) {
+      agg.push_back(gpt_profile_entry{});
+      e = &agg.back();
+      snprintf(e->name, sizeof(e->name), "%s", r.name);
+    }
+    e->calls += 1;
+    e->ms += ms;
+    e->flops += r.flops;
+    e->bytes += r.bytes;
+  }
+  pr.recs.clear();
+  pr.next = 0;
+  const int32_t cap = *count;
+  *count = (int32_t)agg.size();
+  if (out)
+    for (int32_t i = 0; i < std::min(cap, *count); ++i) out[i] = agg[i];
+  return GPT_OK;
 }
 
 gpt_status gpt_destroy(gpt_ctx* ctx) {

@@ -104,3 +104,19 @@ def seeds_for(name: str) -> Dict[str, int]:
         "speedrun-bf16": dict(tokens=5, weights=102, tables=104, trigram=105),
     }
     return table[name]
+
+
+def device_params(cfg: GPTConfig, seed: int, std: float = 0.02, zero_head: bool = False):
+    """Flat parameter buffer drawn on the GPU (torch Philox, seeded): every weight N(0, std),
+    stored in the config's dtype.  Used where host generation of ~2e9 values would dominate."""
+    import torch
+    dt = torch.bfloat16 if cfg.dtype == BF16 else torch.float32
+    flat = torch.zeros(param_elems(cfg), dtype=dt, device="cuda")
+    g = torch.Generator(device="cuda")
+    for i, (name, off, shape) in enumerate(param_layout(cfg)):
+        n = int(np.prod(shape))
+        if zero_head and name == "lm_head":
+            continue
+        g.manual_seed(seed * 1000 + i)
+        flat[off:off + n] = (torch.randn(n, device="cuda", generator=g) * std).to(dt)
+    return flat

@@ -121,6 +121,24 @@ gpt_status gpt_fwd_bwd(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targe
  * Synchronises `stream`, then clears the flags.  flags [host]. */
 gpt_status gpt_check_errors(gpt_ctx* ctx, hipStream_t stream, int32_t* flags);
 
+/* Per-stage timing of gpt_fwd_bwd.  gpt_profile(ctx, 1) makes later steps bracket every launch
+ * with two HIP events on the step's stream (a small overhead per launch); gpt_profile(ctx, 0)
+ * stops recording.  gpt_profile_read synchronises on the recorded events, aggregates them by
+ * stage name in order of first launch, clears them, and writes up to *count entries to `out`
+ * [host] (*count [host] in: capacity, out: number of stages; out may be NULL to query).
+ * flops and bytes are the stage's algorithmic work: 2*M*N*K per GEMM; causal attention
+ * 4*pairs*hd forward, 8*pairs*hd for dK/dV and 2*pairs*hd for dQ (its recomputation of the
+ * scores is not counted); and the bytes each memory-bound kernel must read and write once. */
+typedef struct {
+  char name[32];
+  int32_t calls;
+  float ms;
+  double flops;
+  double bytes;
+} gpt_profile_entry;
+gpt_status gpt_profile(gpt_ctx* ctx, int32_t enable);
+gpt_status gpt_profile_read(gpt_ctx* ctx, gpt_profile_entry* out, int32_t* count);
+
 gpt_status gpt_destroy(gpt_ctx* ctx);
 
 /* Hashed n-gram gather-add (decoder-rtx bigram/trigram tables).  For each sequence b and
