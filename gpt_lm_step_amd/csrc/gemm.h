@@ -28,13 +28,33 @@
 
 namespace gpt {
 
+// Epilogues receive 4 consecutive columns c..c+3 of one output row r (c is a multiple of 4).
+template <typename T> struct Vec4T;
+template <> struct Vec4T<bf16> { typedef bf16x4 type; };
+template <> struct Vec4T<float> { typedef f32x4 type; };
+template <typename T> using vec4t = typename Vec4T<T>::type;
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const float (&v)[4]) {
+  vec4t<T> o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = from_f32<T>(v[i]);
+  *reinterpret_cast<vec4t<T>*>(p) = o;
+}
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, float (&v)[4]) {
+  const vec4t<T> x = *reinterpret_cast<const vec4t<T>*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = to_f32(x[i]);
+}
+
 // out = T(acc)
 template <typename T>
 struct EpiStore {
   T* out;
   long long ldo;
-  __device__ __forceinline__ void operator()(int r, int c, float v) const {
-    out[(long long)r * ldo + c] = from_f32<T>(v);
+  __device__ __forceinline__ void operator()(int r, int c, const float (&v)[4]) const {
+    store4(out + (long long)r * ldo + c, v);
   }
 };
 
@@ -43,9 +63,16 @@ struct EpiStoreF32 {
   float* out;
   long long ldo;
   int beta;
-  __device__ __forceinline__ void operator()(int r, int c, float v) const {
+  __device__ __forceinline__ void operator()(int r, int c, const float (&v)[4]) const {
     float* p = out + (long long)r * ldo + c;
-    *p = beta ? *p + v : v;
+    float o[4] = {v[0], v[1], v[2], v[3]};
+    if (beta) {
+      float old[4];
+      load4(p, old);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] += old[i];
+    }
+    store4(p, o);
   }
 };
 
@@ -54,9 +81,13 @@ struct EpiResid {
   const float* res;
   float* out;
   long long ld;
-  __device__ __forceinline__ void operator()(int r, int c, float v) const {
+  __device__ __forceinline__ void operator()(int r, int c, const float (&v)[4]) const {
     const long long i = (long long)r * ld + c;
-    out[i] = res[i] + v;
+    float o[4];
+    load4(res + i, o);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] += v[k];
+    store4(out + i, o);
   }
 };
 
@@ -68,9 +99,15 @@ struct EpiQKV {
   const float* u;
   long long ldu;
   int vcol0;
-  __device__ __forceinline__ void operator()(int r, int c, float v) const {
-    if (u && c >= vcol0) v += u[(long long)r * ldu + (c - vcol0)];
-    out[(long long)r * ldo + c] = from_f32<T>(v);
+  __device__ __forceinline__ void operator()(int r, int c, const float (&v)[4]) const {
+    float o[4] = {v[0], v[1], v[2], v[3]};
+    if (u && c >= vcol0) {
+      float a[4];
+      load4(u + (long long)r * ldu + (c - vcol0), a);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] += a[k];
+    }
+    store4(out + (long long)r * ldo + c, o);
   }
 };
 
@@ -80,11 +117,16 @@ struct EpiRelu2 {
   T* hp;
   T* act;
   long long ld;
-  __device__ __forceinline__ void operator()(int r, int c, float v) const {
+  __device__ __forceinline__ void operator()(int r, int c, const float (&v)[4]) const {
     const long long i = (long long)r * ld + c;
-    hp[i] = from_f32<T>(v);
-    const float m = v > 0.f ? v : 0.f;
-    act[i] = from_f32<T>(m * m);
+    float a[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float m = v[k] > 0.f ? v[k] : 0.f;
+      a[k] = m * m;
+    }
+    store4(hp + i, v);
+    store4(act + i, a);
   }
 };
 
@@ -94,10 +136,13 @@ struct EpiDRelu2 {
   const T* hp;
   T* out;
   long long ld;
-  __device__ __forceinline__ void operator()(int r, int c, float v) const {
+  __device__ __forceinline__ void operator()(int r, int c, const float (&v)[4]) const {
     const long long i = (long long)r * ld + c;
-    const float h = to_f32(hp[i]);
-    out[i] = from_f32<T>(h > 0.f ? 2.f * h * v : 0.f);
+    float h[4], o[4];
+    load4(hp + i, h);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = h[k] > 0.f ? 2.f * h[k] * v[k] : 0.f;
+    store4(out + i, o);
   }
 };
 
@@ -107,9 +152,16 @@ struct EpiAddRows {
   const T* add;
   float* out;
   long long ld;
-  __device__ __forceinline__ void operator()(int r, int c, float v) const {
+  __device__ __forceinline__ void operator()(int r, int c, const float (&v)[4]) const {
     const long long i = (long long)r * ld + c;
-    out[i] = v + (add ? to_f32(add[i]) : 0.f);
+    float o[4] = {v[0], v[1], v[2], v[3]};
+    if (add) {
+      float a[4];
+      load4(add + i, a);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] += a[k];
+    }
+    store4(out + i, o);
   }
 };
 
@@ -122,7 +174,7 @@ enum GemmSite {
 
 namespace gemm_detail {
 
-constexpr int BM = 128, BN = 128, THREADS = 256;
+constexpr int THREADS = 256;  // 4 waves in a 2 x 2 grid; each wave owns a (BM/2) x (BN/2) tile
 
 template <typename T> struct Mma;
 template <> struct Mma<bf16> {
@@ -144,18 +196,47 @@ struct Cfg {
   static constexpr int KV = BK / 8;                       // 8-element vectors per tile row
 };
 
-// Global -> registers -> LDS staging of one ROWS x BK operand tile.
+// Buffer resource over [base, base + bytes) (bytes <= 2^31): raw loads past the end read 0.
+constexpr uint32_t OOB = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ vec8_t<T> bload8(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(vec8_t<T>, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  } else {
+    const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u, 0, 0);
+    typedef unsigned int u32x8 __attribute__((ext_vector_type(8)));
+    u32x8 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = lo[i];
+      v[4 + i] = hi[i];
+    }
+    return __builtin_bit_cast(vec8_t<T>, v);
+  }
+}
+
+// Global -> registers -> LDS staging of one ROWS x BK operand tile.  KC tiles: thread v moves
+// 16 B vector v (row v / KV, chunk v % KV).  RC tiles: thread t moves the 8 x 8 block
+// (k-chunk t % (BK/8), row block t / (BK/8)): each global load instruction still reads whole
+// 128-byte row segments, and the transposed LDS writes of neighbouring threads fall in distinct
+// banks (row pitch 144 B).
 template <typename T, int ROWS, bool KC>
 struct Stage {
   using C = Cfg<T>;
   using V = vec8_t<T>;
   static constexpr int NVEC = ROWS * C::KV;                       // KC: vectors per tile
-  static constexpr int PER = KC ? (NVEC + THREADS - 1) / THREADS : 8;
   static constexpr int NBLK = (C::BK / 8) * (ROWS / 8);           // RC: 8x8 blocks per tile
-  static_assert(KC || NBLK <= THREADS, "one 8x8 block per thread at most");
+  static constexpr int PER = KC ? (NVEC + THREADS - 1) / THREADS : 8 * ((NBLK + THREADS - 1) / THREADS);
   V r[PER];
 
-  __device__ __forceinline__ void load(const T* __restrict__ p, long long ld, int row0, int k0,
+  // Branch-free loads through a buffer resource: an element outside [0, rows_lim) x [0, k_lim)
+  // gets an offset past the resource's end, which the hardware returns as zeros.
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, long long ld, int row0, int k0,
                                        int rows_lim, int k_lim) {
     const int tid = threadIdx.x;
     if constexpr (KC) {
@@ -163,18 +244,20 @@ struct Stage {
       for (int i = 0; i < PER; ++i) {
         const int v = tid + i * THREADS;
         const int row = row0 + v / C::KV, k = k0 + (v % C::KV) * 8;
-        if (v < NVEC && row < rows_lim && k < k_lim) r[i] = load8(p + (long long)row * ld + k);
-        else r[i] = V{};
+        const bool ok = v < NVEC && row < rows_lim && k < k_lim;
+        r[i] = bload8<T>(rs, ok ? (uint32_t)(((long long)row * ld + k) * sizeof(T)) : OOB);
       }
     } else {
-      if (tid < NBLK) {
-        const int kb = tid / (ROWS / 8), rb = tid % (ROWS / 8);
+#pragma unroll
+      for (int j = 0; j < PER / 8; ++j) {
+        const int blk = tid + j * THREADS;
+        const int kb = blk % (C::BK / 8), rb = blk / (C::BK / 8);
         const int row = row0 + rb * 8;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
           const int k = k0 + kb * 8 + kk;
-          if (row < rows_lim && k < k_lim) r[kk] = load8(p + (long long)k * ld + row);
-          else r[kk] = V{};
+          const bool ok = blk < NBLK && row < rows_lim && k < k_lim;
+          r[j * 8 + kk] = bload8<T>(rs, ok ? (uint32_t)(((long long)k * ld + row) * sizeof(T)) : OOB);
         }
       }
     }
@@ -186,16 +269,19 @@ struct Stage {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         const int v = tid + i * THREADS;
-        if (v < NVEC) store8(lds + (v / C::KV) * C::PITCH + (v % C::KV) * 8, r[i]);
+        if (NVEC % THREADS == 0 || v < NVEC) store8(lds + (v / C::KV) * C::PITCH + (v % C::KV) * 8, r[i]);
       }
     } else {
-      if (tid < NBLK) {
-        const int kb = tid / (ROWS / 8), rb = tid % (ROWS / 8);
+#pragma unroll
+      for (int j = 0; j < PER / 8; ++j) {
+        const int blk = tid + j * THREADS;
+        if (NBLK % THREADS != 0 && blk >= NBLK) continue;
+        const int kb = blk % (C::BK / 8), rb = blk / (C::BK / 8);
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
           V o;
 #pragma unroll
-          for (int kk = 0; kk < 8; ++kk) o[kk] = r[kk][rr];
+          for (int kk = 0; kk < 8; ++kk) o[kk] = r[j * 8 + kk][rr];
           store8(lds + (rb * 8 + rr) * C::PITCH + kb * 8, o);
         }
       }
@@ -219,97 +305,147 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   tn = in / gm;
 }
 
-template <typename T, bool A_KC, bool B_KC, class Epi, int SITE>
-__global__ __launch_bounds__(THREADS, 2) void gemm_kernel(const T* __restrict__ A, long long lda,
-                                                          const T* __restrict__ B, long long ldb,
-                                                          int M, int N, int K, Epi epi) {
+// BM x BN output tile per workgroup; each wave computes (BM/2) x (BN/2) as (BM/64) x (BN/64)
+// MFMA tiles of 32 x 32, so every 16-wide K slice reads BM/64 + BN/64 fragments from LDS for
+// (BM/64) * (BN/64) MFMAs.  The 256 x 256 tile keeps 256 accumulators per lane (AGPRs) and
+// runs one workgroup per CU with both LDS buffers (147 KB).
+template <typename T, int BM, int BN, bool A_KC, bool B_KC, class Epi, int SITE>
+__global__ __launch_bounds__(THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_kernel(
+    const T* __restrict__ A, long long lda, const T* __restrict__ B, long long ldb, int M, int N,
+    int K, uint32_t a_bytes, uint32_t b_bytes, Epi epi) {
   using C = Cfg<T>;
+  constexpr int TM = BM / 64, TN = BN / 64;  // MFMA tiles per wave
   __shared__ __attribute__((aligned(16))) T lds[2][(BM + BN) * C::PITCH];
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE;
-  const int wm = (w / 2) * 64, wn = (w % 2) * 64;
+  const int wm = (w / 2) * (BM / 2), wn = (w % 2) * (BN / 2);
   const int lr = lane % 32, lg = lane / 32;
 
   Stage<T, BM, A_KC> sa;
   Stage<T, BN, B_KC> sb;
-  f32x16 acc[2][2];
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, a_bytes), rb = make_rsrc(B, b_bytes);
+  f32x16 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
   const int nk = (K + C::BK - 1) / C::BK;
-  sa.load(A, lda, m0, 0, M, K);
-  sb.load(B, ldb, n0, 0, N, K);
+  sa.load(ra, lda, m0, 0, M, K);
+  sb.load(rb, ldb, n0, 0, N, K);
   sa.store(lds[0]);
   sb.store(lds[0] + BM * C::PITCH);
+  sa.load(ra, lda, m0, C::BK, M, K);  // loads past K are predicated off (zeros)
+  sb.load(rb, ldb, n0, C::BK, N, K);
   __syncthreads();
 
+  // One barrier per K tile.  Each iteration first writes tile kt+1 (loaded one iteration ago)
+  // into the idle buffer `cur ^ 1` and issues the loads of tile kt+2, then multiplies buffer
+  // `cur`: global latency is hidden behind a full tile of MFMAs.  The scheduling fence keeps
+  // the loads from sinking to the end of the loop.  On the last tiles the stores write unused
+  // data and the loads are predicated off.
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      sa.load(A, lda, m0, (kt + 1) * C::BK, M, K);
-      sb.load(B, ldb, n0, (kt + 1) * C::BK, N, K);
-    }
+    sa.store(lds[cur ^ 1]);
+    sb.store(lds[cur ^ 1] + BM * C::PITCH);
+    sa.load(ra, lda, m0, (kt + 2) * C::BK, M, K);
+    sb.load(rb, ldb, n0, (kt + 2) * C::BK, N, K);
+    __builtin_amdgcn_sched_barrier(0);
     const T* As = lds[cur];
     const T* Bs = lds[cur] + BM * C::PITCH;
 #pragma unroll
     for (int ks = 0; ks < C::BK; ks += 16) {
-      vec8_t<T> af[2], bfr[2];
+      vec8_t<T> af[TM], bfr[TN];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = load8(As + (wm + i * 32 + lr) * C::PITCH + ks + lg * 8);
+      for (int i = 0; i < TM; ++i) af[i] = load8(As + (wm + i * 32 + lr) * C::PITCH + ks + lg * 8);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bfr[j] = load8(Bs + (wn + j * 32 + lr) * C::PITCH + ks + lg * 8);
+      for (int j = 0; j < TN; ++j) bfr[j] = load8(Bs + (wn + j * 32 + lr) * C::PITCH + ks + lg * 8);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) Mma<T>::run(acc[i][j], af[i], bfr[j]);
-    }
-    if (kt + 1 < nk) {
-      sa.store(lds[cur ^ 1]);
-      sb.store(lds[cur ^ 1] + BM * C::PITCH);
+        for (int j = 0; j < TN; ++j) Mma<T>::run(acc[i][j], bfr[j], af[i]);
     }
     __syncthreads();
   }
 
-  // C layout of a 32x32 MFMA tile: lane l, register r -> row (r/4)*8 + (l/32)*4 + r%4, col l%32.
+  // The MFMA computed each 32 x 32 tile transposed (B fragment first), so its output layout
+  // gives lane l output row l%32 and, in registers 4q..4q+3, the four consecutive columns
+  // q*8 + (l/32)*4 + 0..3: the epilogue moves 4 columns per access.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i) {
+    const int row = m0 + wm + i * 32 + lr;
+    if (row >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn + j * 32 + lr;
-      if (col >= N) continue;
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm + i * 32 + (r / 4) * 8 + lg * 4 + (r % 4);
-        if (row < M) epi(row, col, acc[i][j][r]);
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + wn + j * 32 + q * 8 + lg * 4;
+        if (col < N) {
+          const float v[4] = {acc[i][j][q * 4], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2],
+                              acc[i][j][q * 4 + 3]};
+          epi(row, col, v);
+        }
       }
-    }
+  }
+}
+
+// Bytes spanned by an operand of `rows` x K (KC: rows of ld; RC: K rows of ld).
+inline long long operand_bytes(bool kc, long long rows, long long K, long long ld, long long es) {
+  return (kc ? (rows - 1) * ld + K : (K - 1) * ld + rows) * es;
+}
+
+template <typename T, int BM, int BN, class Epi, int SITE>
+void launch_tiles(bool a_kc, bool b_kc, int M, int N, int K, const T* A, long long lda,
+                  const T* B, long long ldb, const Epi& epi, hipStream_t s) {
+  dim3 grid((unsigned)(cdiv(M, BM) * cdiv(N, BN)));
+  const uint32_t ab = (uint32_t)operand_bytes(a_kc, M, K, lda, sizeof(T));
+  const uint32_t bb = (uint32_t)operand_bytes(b_kc, N, K, ldb, sizeof(T));
+#define GEMM_GO(AK, BK_)                                                                        \
+  gemm_kernel<T, BM, BN, AK, BK_, Epi, SITE><<<grid, THREADS, 0, s>>>(A, lda, B, ldb, M, N, K, ab, \
+                                                                     bb, epi)
+  if (a_kc && b_kc) GEMM_GO(true, true);
+  else if (a_kc) GEMM_GO(true, false);
+  else if (b_kc) GEMM_GO(false, true);
+  else GEMM_GO(false, false);
+#undef GEMM_GO
 }
 
 }  // namespace gemm_detail
 
+// C[m,n] = sum_k A(m,k) B(n,k); a_kc/b_kc select K-contiguous (p[r*ld+k]) or row-contiguous
+// (p[k*ld+r]) operands.  Requirements: K % 8 == 0, lda/ldb % 8 == 0, 16-byte aligned operands,
+// M % 8 == 0 for a row-contiguous A, N % 8 == 0 for a row-contiguous B, N % 4 == 0 and output
+// leading dimensions (inside the epilogue) multiples of 4.  bf16 problems whose
+// 256 x 256 tiling fills the GPU (>= 240 tiles for 256 CUs) use that tile, the rest 128 x 128;
+// fp32 uses 64 x 64.
 template <int SITE, typename T, class Epi>
-inline gpt_status gemm(bool a_kc, bool b_kc, int M, int N, int K, const T* A, long long lda, const T* B,
-                long long ldb, const Epi& epi, hipStream_t s) {
+inline gpt_status gemm(bool a_kc, bool b_kc, int M, int N, int K, const T* A, long long lda,
+                       const T* B, long long ldb, const Epi& epi, hipStream_t s) {
   if (M <= 0 || N <= 0) return GPT_OK;
   if (K <= 0 || K % 8) return fail(GPT_ESHAPE, "gemm: K must be a positive multiple of 8");
   if (lda % 8 || ldb % 8) return fail(GPT_ESHAPE, "gemm: leading dimensions must be multiples of 8");
   if ((!a_kc && M % 8) || (!b_kc && N % 8))
     return fail(GPT_ESHAPE, "gemm: row-contiguous operands need a multiple of 8 rows");
+  if (N % 4) return fail(GPT_ESHAPE, "gemm: N must be a multiple of 4");
   if (((uintptr_t)A | (uintptr_t)B) % 16) return fail(GPT_EINVAL, "gemm: operands must be 16-byte aligned");
-  const long long tiles = (long long)cdiv(M, gemm_detail::BM) * cdiv(N, gemm_detail::BN);
-  if (tiles >= (1LL << 31)) return fail(GPT_ESHAPE, "gemm: too many tiles");
-  dim3 grid((unsigned)tiles);
-  if (a_kc && b_kc) gemm_detail::gemm_kernel<T, true, true, Epi, SITE><<<grid, gemm_detail::THREADS, 0, s>>>(A, lda, B, ldb, M, N, K, epi);
-  else if (a_kc) gemm_detail::gemm_kernel<T, true, false, Epi, SITE><<<grid, gemm_detail::THREADS, 0, s>>>(A, lda, B, ldb, M, N, K, epi);
-  else if (b_kc) gemm_detail::gemm_kernel<T, false, true, Epi, SITE><<<grid, gemm_detail::THREADS, 0, s>>>(A, lda, B, ldb, M, N, K, epi);
-  else gemm_detail::gemm_kernel<T, false, false, Epi, SITE><<<grid, gemm_detail::THREADS, 0, s>>>(A, lda, B, ldb, M, N, K, epi);
+  if (gemm_detail::operand_bytes(a_kc, M, K, lda, sizeof(T)) > (1LL << 31) ||
+      gemm_detail::operand_bytes(b_kc, N, K, ldb, sizeof(T)) > (1LL << 31))
+    return fail(GPT_ESHAPE, "gemm: each operand must span at most 2 GiB");
+  const long long big_tiles = (long long)cdiv(M, 256) * cdiv(N, 256);
+  if ((long long)cdiv(M, 128) * cdiv(N, 128) >= (1LL << 31)) return fail(GPT_ESHAPE, "gemm: too many tiles");
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (big_tiles >= 240)
+      gemm_detail::launch_tiles<T, 256, 256, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
+    else
+      gemm_detail::launch_tiles<T, 128, 128, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
+  } else {
+    // fp32 serves the small parity configurations only
+    gemm_detail::launch_tiles<T, 64, 64, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
+  }
   return check_launch("gemm");
 }
-
 
 }  // namespace gpt

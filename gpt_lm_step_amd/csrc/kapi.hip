@@ -15,7 +15,8 @@ gpt_status gptk_gemm(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32
                      const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
                      int64_t ldc, int32_t beta, hipStream_t stream) {
   if (bad_dtype(dtype) || !A || !B || !C) return fail(GPT_EINVAL, "gptk_gemm: bad dtype or null");
-  if (M < 0 || N < 0 || K < 0 || ldc < N) return fail(GPT_ESHAPE, "gptk_gemm: bad sizes");
+  if (M < 0 || N < 0 || K < 0 || ldc < N || ldc % 4) return fail(GPT_ESHAPE, "gptk_gemm: bad sizes");
+  if (((uintptr_t)C) % 16) return fail(GPT_EINVAL, "gptk_gemm: C must be 16-byte aligned");
   EpiStoreF32 epi{C, ldc, beta ? 1 : 0};
   if (dtype == GPT_BF16)
     return gemm<G_TEST, bf16>(a_kc, b_kc, M, N, K, (const bf16*)A, lda, (const bf16*)B, ldb, epi, stream);

@@ -75,11 +75,12 @@ gpt_status validate(const gpt_config* c) {
 }
 
 
-// Tokens of one head/cross-entropy chunk: all tokens when the bf16/fp32 logits fit in 4 GiB.
+// Tokens of one head/cross-entropy chunk: all tokens when the bf16/fp32 logits fit in 2 GiB
+// (the most one GEMM operand may span).
 long long ce_chunk_rows(const gpt_config& c) {
   const long long N = (long long)c.batch * c.seq_len;
   const long long esz = c.dtype == GPT_BF16 ? 2 : 4;
-  long long rows = (4LL << 30) / ((long long)c.vocab * esz);
+  long long rows = (2LL << 30) / ((long long)c.vocab * esz);
   rows = std::max<long long>(64, rows / 64 * 64);
   return std::min(N, rows);
 }

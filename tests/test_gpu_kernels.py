@@ -42,6 +42,18 @@ def test_gemm_layouts(dtype, a_kc, b_kc, M, N, K):
     assert rel_l2(host(c), 2 * want) < tol
 
 
+@pytest.mark.parametrize("a_kc,b_kc", [(1, 1), (1, 0), (0, 0), (0, 1)])
+def test_gemm_big_tile_ragged(a_kc, b_kc):
+    """Enough 256 x 256 tiles to select the large-tile kernel, with ragged M, N and K tails."""
+    M, N, K = 4104, 3848, 264
+    a, ta = _operand(21, M, K, a_kc, BF)
+    b, tb = _operand(22, N, K, b_kc, BF)
+    c = torch.full((M, N), float("nan"), device="cuda")
+    B.gptk_gemm(a_kc, b_kc, M, N, K, ta, K if a_kc else M, tb, K if b_kc else N, c, N)
+    want = a.astype(np.float64) @ b.astype(np.float64).T
+    assert rel_l2(host(c), want) < 1e-5
+
+
 def test_gemm_large_square_bf16():
     M = N = K = 2048
     a, ta = _operand(3, M, K, 1, BF)
