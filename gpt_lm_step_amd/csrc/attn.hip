@@ -75,38 +75,78 @@ __device__ __forceinline__ vec8_t<T> acc_frag(const f32x16& acc, int h) {
   return v;
 }
 
-// Rows [r0, r0+R) x HD columns of a matrix with row stride ld -> lds[r][d] (rows >= lim: 0).
-template <typename T, int R, int HD>
-__device__ __forceinline__ void stage_rows(T* lds, int pitch, const T* __restrict__ g,
-                                           long long ld, int r0, int lim) {
-  constexpr int NV = R * HD / 8;
-  for (int v = threadIdx.x; v < NV; v += ATHREADS) {
-    const int r = v / (HD / 8), c = (v % (HD / 8)) * 8;
-    vec8_t<T> x = (r0 + r < lim) ? load8(g + (long long)(r0 + r) * ld + c) : vec8_t<T>{};
-    store8(lds + r * pitch + c, x);
+// 2^x with the hardware instruction (v_exp_f32; results below 2^-126 flush to 0, 2^-inf = 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Buffer resource over [base, base + bytes): raw loads past the end read as zeros, so tiles that
+// run past the sequence need no branches.
+constexpr uint32_t OOB = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x8 __attribute__((ext_vector_type(8)));
+template <typename T>
+__device__ __forceinline__ vec8_t<T> bload8(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(vec8_t<T>, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  } else {
+    const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u, 0, 0);
+    u32x8 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = lo[i];
+      v[4 + i] = hi[i];
+    }
+    return __builtin_bit_cast(vec8_t<T>, v);
   }
 }
-// Same rows, transposed: lds[d][r].
+
+// One R x HD tile of a token-major matrix (rows of `ld` elements) moved global -> registers ->
+// LDS as 8 x 8 blocks by the (R/8)*(HD/8) threads t in [0, NB).  A block can be written in row
+// layout lds[r][d] and/or transposed lds[d][r].  ROWFAST maps consecutive threads to consecutive
+// row blocks (conflict-free transposed writes), otherwise to consecutive column blocks
+// (conflict-free row writes); either way each global load instruction reads whole row segments.
 template <typename T, int R, int HD>
-__device__ __forceinline__ void stage_transposed(T* lds, int pitch, const T* __restrict__ g,
-                                                 long long ld, int r0, int lim) {
-  constexpr int NB = (R / 8) * (HD / 8);
-  for (int b = threadIdx.x; b < NB; b += ATHREADS) {
-    const int rb = b % (R / 8), db = b / (R / 8);
-    vec8_t<T> in[8];
+struct Tile88 {
+  static constexpr int NB = (R / 8) * (HD / 8);
+  vec8_t<T> r[8];
+  int rb, cb;
+  bool active;
+  __device__ __forceinline__ void init(int t, bool rowfast) {
+    active = t >= 0 && t < NB;
+    rb = rowfast ? t % (R / 8) : t / (HD / 8);
+    cb = rowfast ? t / (R / 8) : t % (HD / 8);
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, long long ld, int row0, int lim) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int r = r0 + rb * 8 + k;
-      in[k] = (r < lim) ? load8(g + (long long)r * ld + db * 8) : vec8_t<T>{};
+      const int row = row0 + rb * 8 + k;
+      const bool ok = active && row < lim;
+      r[k] = bload8<T>(rs, ok ? (uint32_t)(((long long)row * ld + cb * 8) * sizeof(T)) : OOB);
     }
+  }
+  __device__ __forceinline__ void store_rows(T* lds, int pitch) const {
+    if (!active) return;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) store8(lds + (rb * 8 + k) * pitch + cb * 8, r[k]);
+  }
+  __device__ __forceinline__ void store_trans(T* lds, int pitch) const {
+    if (!active) return;
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       vec8_t<T> o;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) o[k] = in[k][d];
-      store8(lds + (db * 8 + d) * pitch + rb * 8, o);
+      for (int k = 0; k < 8; ++k) o[k] = r[k][d];
+      store8(lds + (cb * 8 + d) * pitch + rb * 8, o);
     }
   }
+};
+
+template <typename T>
+__device__ __forceinline__ uint32_t span_bytes(int Tn, long long ld, int hd) {
+  return (uint32_t)(((long long)(Tn - 1) * ld + hd) * sizeof(T));
 }
 
 // Output of a [HD x 32] transposed accumulator set (lane = row l%32 of the result) stored as
@@ -126,96 +166,139 @@ __device__ __forceinline__ void store_acc_rows(T* __restrict__ dst_row, const f3
 }
 
 // ------------------------------------------------------------------ forward
-template <typename T, int HD>
-__global__ __launch_bounds__(ATHREADS, 2) void attn_fwd_kernel(const T* __restrict__ qkv,
-                                                               T* __restrict__ out,
-                                                               float* __restrict__ lse2,
-                                                               int Tn, int H, float sl2) {
-  constexpr int BKV = 64, PK = HD + pad<T>(), PV = BKV + pad<T>();
-  __shared__ __attribute__((aligned(16))) T Ks[BKV * PK];
-  __shared__ __attribute__((aligned(16))) T Vt[HD * PV];
+// Workgroup: 4 waves x QSUB 32-query sub-tiles (with QSUB = 2, wave w takes sub-tiles w and
+// 7 - w, pairing light and heavy rows of the causal triangle).  K/V tiles of 64 keys are double
+// buffered in LDS: each iteration writes tile j+1 (held in registers) and loads tile j+2 before
+// multiplying tile j.  Threads 0..127 move K (row layout), 128..255 move V (transposed).
+template <typename T, int HD, int QSUB>
+__global__ __launch_bounds__(ATHREADS, QSUB == 2 ? 1 : 2) void attn_fwd_kernel(
+    const T* __restrict__ qkv, T* __restrict__ out, float* __restrict__ lse2, int Tn, int H,
+    float sl2) {
+  constexpr int BKV = 64, BQ = 128 * QSUB, PK = HD + pad<T>(), PV = BKV + pad<T>();
+  __shared__ __attribute__((aligned(16))) T Ks[2][BKV * PK];
+  __shared__ __attribute__((aligned(16))) T Vt[2][HD * PV];
   const int D = H * HD;
   const long long ld = 3LL * D;
   const int qb = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE, lr = lane % 32, g = lane / 32;
-  const int q0 = qb * 128 + w * 32, q = q0 + lr;
-  const bool active = q0 < Tn;
   const T* base = qkv + (long long)b * Tn * ld;
 
-  vec8_t<T> qf[HD / 16];
-  if (active) {
+  int q0[QSUB];
+  vec8_t<T> qf[QSUB][HD / 16];
+  f32x16 o[QSUB][HD / 32];
+  float m[QSUB], l[QSUB];
 #pragma unroll
-    for (int c = 0; c < HD / 16; ++c) qf[c] = load8(base + (long long)q * ld + h * HD + c * 16 + g * 8);
+  for (int s = 0; s < QSUB; ++s) {
+    const int sub = QSUB == 2 ? (s == 0 ? w : 7 - w) : w;
+    q0[s] = qb * BQ + sub * 32;
+    const int q = min(q0[s] + lr, Tn - 1);
+#pragma unroll
+    for (int c = 0; c < HD / 16; ++c) qf[s][c] = load8(base + (long long)q * ld + h * HD + c * 16 + g * 8);
+#pragma unroll
+    for (int i = 0; i < HD / 32; ++i) o[s][i] = f32x16{};
+    m[s] = -INFINITY;
+    l[s] = 0.f;
   }
-  f32x16 o[HD / 32];
-#pragma unroll
-  for (int i = 0; i < HD / 32; ++i) o[i] = f32x16{};
-  float m = -INFINITY, l = 0.f;
 
-  const int kv_end = min(Tn, (qb + 1) * 128);
-  for (int kv0 = 0; kv0 < kv_end; kv0 += BKV) {
-    __syncthreads();
-    stage_rows<T, BKV, HD>(Ks, PK, base + D + h * HD, ld, kv0, Tn);
-    stage_transposed<T, BKV, HD>(Vt, PV, base + 2 * D + h * HD, ld, kv0, Tn);
-    __syncthreads();
-    if (!active || kv0 > q0 + 31) continue;
-    f32x16 s[2];
+  const bool is_v = threadIdx.x >= 128;
+  Tile88<T, BKV, HD> st;
+  st.init(is_v ? threadIdx.x - 128 : threadIdx.x, is_v);
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(base + (is_v ? 2 * D : D) + h * HD, span_bytes<T>(Tn, ld, HD));
+  auto put = [&](int buf) {
+    if (is_v) st.store_trans(Vt[buf], PV);
+    else st.store_rows(Ks[buf], PK);
+  };
+  const int nkv = (min(Tn, (qb + 1) * BQ) - 1) / BKV + 1;
+  st.load(rs, ld, 0, Tn);
+  put(0);
+  st.load(rs, ld, BKV, Tn);
+  __syncthreads();
+
+  for (int j = 0; j < nkv; ++j) {
+    const int cur = j & 1, kv0 = j * BKV;
+    put(cur ^ 1);
+    st.load(rs, ld, (j + 2) * BKV, Tn);
+    __builtin_amdgcn_sched_barrier(0);
+    const T* K_ = Ks[cur];
+    const T* V_ = Vt[cur];
+    // Scores are kept unscaled; the row max m is in the same unit, and the softmax weight is
+    // 2^(sl2 * (s - m)) (sl2 = log2(e) / sqrt(Hd)).  Only the tile that crosses the diagonal
+    // evaluates the causal mask.
+    auto tile = [&](auto diag_c, int s) {
+      constexpr bool DIAG = decltype(diag_c)::value;
+      const int q = q0[s] + lr;
+      f32x16 sc[2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      s[st] = f32x16{};
+      for (int st2 = 0; st2 < 2; ++st2) {
+        sc[st2] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < HD / 16; ++c) mma<T>(s[st], frag_rows(Ks, PK, st * 32 + lr, c * 16, g), qf[c]);
-    }
-    const bool diag = kv0 + BKV - 1 > q0;
-    float mx = -INFINITY;
+        for (int c = 0; c < HD / 16; ++c) mma<T>(sc[st2], frag_rows(K_, PK, st2 * 32 + lr, c * 16, g), qf[s][c]);
+      }
+      float mx = -INFINITY;
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int st2 = 0; st2 < 2; ++st2)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = s[st][r] * sl2;
-        if (diag) {
-          const int key = kv0 + st * 32 + (r / 4) * 8 + g * 4 + (r % 4);
-          if (key > q) v = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          if (DIAG) {
+            const int key = kv0 + st2 * 32 + (r / 4) * 8 + g * 4 + (r % 4);
+            if (key > q) sc[st2][r] = -INFINITY;
+          }
+          mx = fmaxf(mx, sc[st2][r]);
         }
-        s[st][r] = v;
-        mx = fmaxf(mx, v);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+      const float mn = fmaxf(m[s], mx);
+      const float nb = -mn * sl2;
+      float sum = 0.f;
+#pragma unroll
+      for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = fast_exp2(fmaf(sc[st2][r], sl2, nb));
+          sc[st2][r] = pv;
+          sum += pv;
+        }
+      sum += __shfl_xor(sum, 32, WAVE);
+      // rescale the running output only when some row's max moved (rare after the first tiles)
+      if (!__all(mn == m[s])) {
+        const float alpha = fast_exp2((m[s] - mn) * sl2);
+#pragma unroll
+        for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[s][dt][r] *= alpha;
+        l[s] *= alpha;
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-    const float mn = fmaxf(m, mx);
-    const float alpha = exp2f(m - mn);
-    float sum = 0.f;
+      l[s] += sum;
+      m[s] = mn;
+      vec8_t<T> pf[2][2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int st2 = 0; st2 < 2; ++st2)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(s[st][r] - mn);
-        s[st][r] = p;
-        sum += p;
-      }
-    sum += __shfl_xor(sum, 32, WAVE);
-    l = l * alpha + sum;
-    m = mn;
+        for (int hh = 0; hh < 2; ++hh) pf[st2][hh] = acc_frag<T>(sc[st2], hh);
 #pragma unroll
-    for (int dt = 0; dt < HD / 32; ++dt)
+      for (int dt = 0; dt < HD / 32; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    vec8_t<T> pf[2][2];
+        for (int st2 = 0; st2 < 2; ++st2)
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+          for (int hh = 0; hh < 2; ++hh)
+            mma<T>(o[s][dt], frag_split(V_, PV, dt * 32 + lr, st2 * 32 + hh * 16, g), pf[st2][hh]);
+    };
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) pf[st][hh] = acc_frag<T>(s[st], hh);
-#pragma unroll
-    for (int dt = 0; dt < HD / 32; ++dt)
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          mma<T>(o[dt], frag_split(Vt, PV, dt * 32 + lr, st * 32 + hh * 16, g), pf[st][hh]);
+    for (int s = 0; s < QSUB; ++s) {
+      if (q0[s] >= Tn || kv0 > q0[s] + 31) continue;  // wave-uniform
+      if (kv0 + BKV - 1 > q0[s]) tile(std::true_type(), s);
+      else tile(std::false_type(), s);
+    }
+    __syncthreads();
   }
-  if (!active) return;
-  T* dst = out + ((long long)b * Tn + q) * D + h * HD;
-  store_acc_rows<T, HD>(dst, o, 1.f / l, g);
-  if (g == 0) lse2[((long long)b * H + h) * Tn + q] = m + log2f(l);
+#pragma unroll
+  for (int s = 0; s < QSUB; ++s) {
+    if (q0[s] >= Tn) continue;
+    const int q = q0[s] + lr;
+    T* dst = out + ((long long)b * Tn + q) * D + h * HD;
+    store_acc_rows<T, HD>(dst, o[s], 1.f / l[s], g);
+    if (g == 0) lse2[((long long)b * H + h) * Tn + q] = m[s] * sl2 + log2f(l[s]);
+  }
 }
 
 // ------------------------------------------------------------------ backward
@@ -243,18 +326,20 @@ __global__ void attn_bwd_pre_kernel(const T* __restrict__ o, const T* __restrict
   dq_sum[(b * H + h) * Tn + t] = s;
 }
 
-// dK, dV for 128 keys per workgroup (4 waves x 32 keys), looping over 32-query tiles.
+// dK, dV for 128 keys per workgroup (4 waves x 32 keys held in registers), looping over
+// 64-query tiles double buffered in LDS (Q and dO, each in row and transposed layout, plus the
+// tile's LSE and rowsum(dO*O)).  Threads 0..127 move Q, 128..255 move dO.
 template <typename T, int HD>
-__global__ __launch_bounds__(ATHREADS, HD >= 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dkdv_kernel(
     const T* __restrict__ qkv, const T* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ dq_sum, T* __restrict__ dqkv, int Tn, int H, float sl2,
     float scale) {
-  constexpr int BQ = 32, PR = HD + pad<T>(), PT = BQ + pad<T>();
-  __shared__ __attribute__((aligned(16))) T Qs[BQ * PR];
-  __shared__ __attribute__((aligned(16))) T Qt[HD * PT];
-  __shared__ __attribute__((aligned(16))) T Os[BQ * PR];
-  __shared__ __attribute__((aligned(16))) T Ot[HD * PT];
-  __shared__ float lse_s[BQ], dsum_s[BQ];
+  constexpr int BQ = 64, PR = HD + pad<T>(), PT = BQ + pad<T>();
+  __shared__ __attribute__((aligned(16))) T Qs[2][BQ * PR];
+  __shared__ __attribute__((aligned(16))) T Qt[2][HD * PT];
+  __shared__ __attribute__((aligned(16))) T Os[2][BQ * PR];
+  __shared__ __attribute__((aligned(16))) T Ot[2][HD * PT];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][BQ], dsum_s[2][BQ];
   const int D = H * HD;
   const long long ld = 3LL * D;
   const int kb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;  // key block 0 is the heaviest
@@ -267,11 +352,12 @@ __global__ __launch_bounds__(ATHREADS, HD >= 128 ? 1 : 2) void attn_bwd_dkdv_ker
   const float* drow = dq_sum + ((long long)b * H + h) * Tn;
 
   vec8_t<T> kf[HD / 16], vf[HD / 16];
-  if (active) {
+  {
+    const int kk = min(key, Tn - 1);
 #pragma unroll
     for (int c = 0; c < HD / 16; ++c) {
-      kf[c] = load8(base + (long long)key * ld + D + h * HD + c * 16 + g * 8);
-      vf[c] = load8(base + (long long)key * ld + 2 * D + h * HD + c * 16 + g * 8);
+      kf[c] = load8(base + (long long)kk * ld + D + h * HD + c * 16 + g * 8);
+      vf[c] = load8(base + (long long)kk * ld + 2 * D + h * HD + c * 16 + g * 8);
     }
   }
   f32x16 dk[HD / 32], dv[HD / 32];
@@ -280,46 +366,85 @@ __global__ __launch_bounds__(ATHREADS, HD >= 128 ? 1 : 2) void attn_bwd_dkdv_ker
     dk[i] = f32x16{};
     dv[i] = f32x16{};
   }
-  for (int q0 = kb * 128; q0 < Tn; q0 += BQ) {
-    __syncthreads();
-    stage_rows<T, BQ, HD>(Qs, PR, base + h * HD, ld, q0, Tn);
-    stage_transposed<T, BQ, HD>(Qt, PT, base + h * HD, ld, q0, Tn);
-    stage_rows<T, BQ, HD>(Os, PR, dbase + h * HD, D, q0, Tn);
-    stage_transposed<T, BQ, HD>(Ot, PT, dbase + h * HD, D, q0, Tn);
-    if (threadIdx.x < BQ) {
-      lse_s[threadIdx.x] = lrow[q0 + threadIdx.x];
-      dsum_s[threadIdx.x] = drow[q0 + threadIdx.x];
+
+  const bool is_o = threadIdx.x >= 128;
+  const int tl = is_o ? threadIdx.x - 128 : threadIdx.x;
+  Tile88<T, BQ, HD> st;
+  st.init(tl, false);
+  const __amdgpu_buffer_rsrc_t rs = is_o ? make_rsrc(dbase + h * HD, span_bytes<T>(Tn, D, HD))
+                                         : make_rsrc(base + h * HD, span_bytes<T>(Tn, ld, HD));
+  const long long sld = is_o ? (long long)D : ld;
+  float stat = 0.f;  // threads 0..63: LSE of query q_tile + t; 64..127: rowsum(dO*O)
+  auto fetch = [&](int qt) {
+    st.load(rs, sld, qt, Tn);
+    if (threadIdx.x < 2 * BQ) {
+      const int qi = qt + (threadIdx.x % BQ);
+      stat = qi < Tn ? (threadIdx.x < BQ ? lrow[qi] : drow[qi]) : 0.f;
     }
-    __syncthreads();
-    if (!active || q0 + BQ - 1 < k0) continue;
-    f32x16 s = f32x16{}, dp = f32x16{};
+  };
+  auto put = [&](int buf) {
+    st.store_rows(is_o ? Os[buf] : Qs[buf], PR);
+    st.store_trans(is_o ? Ot[buf] : Qt[buf], PT);
+    if (threadIdx.x < BQ) lse_s[buf][threadIdx.x] = stat;
+    else if (threadIdx.x < 2 * BQ) dsum_s[buf][threadIdx.x - BQ] = stat;
+  };
+  const int qstart = kb * 128;
+  const int nq = Tn > qstart ? (Tn - qstart + BQ - 1) / BQ : 0;
+  fetch(qstart);
+  put(0);
+  fetch(qstart + BQ);
+  __syncthreads();
+
+  for (int j = 0; j < nq; ++j) {
+    const int cur = j & 1, qt = qstart + j * BQ;
+    put(cur ^ 1);
+    fetch(qt + 2 * BQ);
+    __builtin_amdgcn_sched_barrier(0);
+    auto sub = [&](auto diag_c, int qs) {
+      constexpr bool DIAG = decltype(diag_c)::value;
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int c = 0; c < HD / 16; ++c) {
-      mma<T>(s, frag_rows(Qs, PR, lr, c * 16, g), kf[c]);
-      mma<T>(dp, frag_rows(Os, PR, lr, c * 16, g), vf[c]);
-    }
-    const bool diag = q0 < k0 + 31;
+      for (int c = 0; c < HD / 16; ++c) {
+        mma<T>(s, frag_rows(Qs[cur], PR, qs * 32 + lr, c * 16, g), kf[c]);
+        mma<T>(dp, frag_rows(Os[cur], PR, qs * 32 + lr, c * 16, g), vf[c]);
+      }
+      // register r holds query qs*32 + (r/4)*8 + g*4 + r%4: statistics come as float4 groups
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qi = (r / 4) * 8 + g * 4 + (r % 4);
-      float p = exp2f(s[r] * sl2 - lse_s[qi]);
-      if (diag && key > q0 + qi) p = 0.f;
-      s[r] = p;
-      dp[r] = p * (dp[r] - dsum_s[qi]);
-    }
-    vec8_t<T> pf[2], sf[2];
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int qb4 = qs * 32 + r4 * 8 + g * 4;
+        const f32x4 ls = *reinterpret_cast<const f32x4*>(&lse_s[cur][qb4]);
+        const f32x4 dsm = *reinterpret_cast<const f32x4*>(&dsum_s[cur][qb4]);
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      pf[hh] = acc_frag<T>(s, hh);
-      sf[hh] = acc_frag<T>(dp, hh);
-    }
-#pragma unroll
-    for (int dt = 0; dt < HD / 32; ++dt)
+        for (int i = 0; i < 4; ++i) {
+          const int r = r4 * 4 + i;
+          float p = fast_exp2(fmaf(s[r], sl2, -ls[i]));
+          if (DIAG && key > qt + qb4 + i) p = 0.f;
+          s[r] = p;
+          dp[r] = p * (dp[r] - dsm[i]);
+        }
+      }
+      vec8_t<T> pf[2], sf[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        mma<T>(dv[dt], frag_split(Ot, PT, dt * 32 + lr, hh * 16, g), pf[hh]);
-        mma<T>(dk[dt], frag_split(Qt, PT, dt * 32 + lr, hh * 16, g), sf[hh]);
+        pf[hh] = acc_frag<T>(s, hh);
+        sf[hh] = acc_frag<T>(dp, hh);
       }
+#pragma unroll
+      for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          mma<T>(dv[dt], frag_split(Ot[cur], PT, dt * 32 + lr, qs * 32 + hh * 16, g), pf[hh]);
+          mma<T>(dk[dt], frag_split(Qt[cur], PT, dt * 32 + lr, qs * 32 + hh * 16, g), sf[hh]);
+        }
+    };
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const int q0 = qt + qs * 32;
+      if (!active || q0 >= Tn || q0 + 31 < k0) continue;  // wave-uniform
+      if (q0 < k0 + 31) sub(std::true_type(), qs);
+      else sub(std::false_type(), qs);
+    }
+    __syncthreads();
   }
   if (!active) return;
   T* row = dqkv + ((long long)b * Tn + key) * ld + h * HD;
@@ -327,16 +452,17 @@ __global__ __launch_bounds__(ATHREADS, HD >= 128 ? 1 : 2) void attn_bwd_dkdv_ker
   store_acc_rows<T, HD>(row + 2 * D, dv, 1.f, g);
 }
 
-// dQ for 128 queries per workgroup, looping over 64-key tiles.
+// dQ for 128 queries per workgroup (4 waves x 32), looping over 64-key tiles double buffered in
+// LDS (K in row and transposed layout, V in row layout).  Threads 0..127 move K, 128..255 V.
 template <typename T, int HD>
-__global__ __launch_bounds__(ATHREADS, 2) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dq_kernel(
     const T* __restrict__ qkv, const T* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ dq_sum, T* __restrict__ dqkv, int Tn, int H, float sl2,
     float scale) {
   constexpr int BKV = 64, PR = HD + pad<T>(), PT = BKV + pad<T>();
-  __shared__ __attribute__((aligned(16))) T Ks[BKV * PR];
-  __shared__ __attribute__((aligned(16))) T Vs[BKV * PR];
-  __shared__ __attribute__((aligned(16))) T Kt[HD * PT];
+  __shared__ __attribute__((aligned(16))) T Ks[2][BKV * PR];
+  __shared__ __attribute__((aligned(16))) T Vs[2][BKV * PR];
+  __shared__ __attribute__((aligned(16))) T Kt[2][HD * PT];
   const int D = H * HD;
   const long long ld = 3LL * D;
   const int qb = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -345,60 +471,86 @@ __global__ __launch_bounds__(ATHREADS, 2) void attn_bwd_dq_kernel(
   const bool active = q0 < Tn;
   const T* base = qkv + (long long)b * Tn * ld;
   vec8_t<T> qf[HD / 16], of[HD / 16];
-  float lq = 0.f, dsum = 0.f;
-  if (active) {
+  float lq, dsum;
+  {
+    const int qq = min(q, Tn - 1);
 #pragma unroll
     for (int c = 0; c < HD / 16; ++c) {
-      qf[c] = load8(base + (long long)q * ld + h * HD + c * 16 + g * 8);
-      of[c] = load8(dout + ((long long)b * Tn + q) * D + h * HD + c * 16 + g * 8);
+      qf[c] = load8(base + (long long)qq * ld + h * HD + c * 16 + g * 8);
+      of[c] = load8(dout + ((long long)b * Tn + qq) * D + h * HD + c * 16 + g * 8);
     }
-    lq = lse2[((long long)b * H + h) * Tn + q];
-    dsum = dq_sum[((long long)b * H + h) * Tn + q];
+    lq = lse2[((long long)b * H + h) * Tn + qq];
+    dsum = dq_sum[((long long)b * H + h) * Tn + qq];
   }
   f32x16 dq[HD / 32];
 #pragma unroll
   for (int i = 0; i < HD / 32; ++i) dq[i] = f32x16{};
-  const int kv_end = min(Tn, (qb + 1) * 128);
-  for (int kv0 = 0; kv0 < kv_end; kv0 += BKV) {
-    __syncthreads();
-    stage_rows<T, BKV, HD>(Ks, PR, base + D + h * HD, ld, kv0, Tn);
-    stage_rows<T, BKV, HD>(Vs, PR, base + 2 * D + h * HD, ld, kv0, Tn);
-    stage_transposed<T, BKV, HD>(Kt, PT, base + D + h * HD, ld, kv0, Tn);
-    __syncthreads();
-    if (!active || kv0 > q0 + 31) continue;
-    const bool diag = kv0 + BKV - 1 > q0;
-    vec8_t<T> sf[2][2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int c = 0; c < HD / 16; ++c) {
-        mma<T>(s, frag_rows(Ks, PR, st * 32 + lr, c * 16, g), qf[c]);
-        mma<T>(dp, frag_rows(Vs, PR, st * 32 + lr, c * 16, g), of[c]);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + st * 32 + (r / 4) * 8 + g * 4 + (r % 4);
-        float p = exp2f(s[r] * sl2 - lq);
-        if (diag && key > q) p = 0.f;
-        dp[r] = p * (dp[r] - dsum);
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) sf[st][hh] = acc_frag<T>(dp, hh);
+
+  const bool is_v = threadIdx.x >= 128;
+  Tile88<T, BKV, HD> st;
+  st.init(is_v ? threadIdx.x - 128 : threadIdx.x, false);
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(base + (is_v ? 2 * D : D) + h * HD, span_bytes<T>(Tn, ld, HD));
+  auto put = [&](int buf) {
+    if (is_v) {
+      st.store_rows(Vs[buf], PR);
+    } else {
+      st.store_rows(Ks[buf], PR);
+      st.store_trans(Kt[buf], PT);
     }
+  };
+  const int nkv = (min(Tn, (qb + 1) * 128) - 1) / BKV + 1;
+  st.load(rs, ld, 0, Tn);
+  put(0);
+  st.load(rs, ld, BKV, Tn);
+  __syncthreads();
+
+  for (int j = 0; j < nkv; ++j) {
+    const int cur = j & 1, kv0 = j * BKV;
+    put(cur ^ 1);
+    st.load(rs, ld, (j + 2) * BKV, Tn);
+    __builtin_amdgcn_sched_barrier(0);
+    auto tile = [&](auto diag_c) {
+      constexpr bool DIAG = decltype(diag_c)::value;
+      vec8_t<T> sf[2][2];
 #pragma unroll
-    for (int dt = 0; dt < HD / 32; ++dt)
+      for (int st2 = 0; st2 < 2; ++st2) {
+        f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+        for (int c = 0; c < HD / 16; ++c) {
+          mma<T>(s, frag_rows(Ks[cur], PR, st2 * 32 + lr, c * 16, g), qf[c]);
+          mma<T>(dp, frag_rows(Vs[cur], PR, st2 * 32 + lr, c * 16, g), of[c]);
+        }
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          mma<T>(dq[dt], frag_split(Kt, PT, dt * 32 + lr, st * 32 + hh * 16, g), sf[st][hh]);
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(fmaf(s[r], sl2, -lq));
+          if (DIAG) {
+            const int key = kv0 + st2 * 32 + (r / 4) * 8 + g * 4 + (r % 4);
+            if (key > q) p = 0.f;
+          }
+          dp[r] = p * (dp[r] - dsum);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) sf[st2][hh] = acc_frag<T>(dp, hh);
+      }
+#pragma unroll
+      for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+        for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+            mma<T>(dq[dt], frag_split(Kt[cur], PT, dt * 32 + lr, st2 * 32 + hh * 16, g), sf[st2][hh]);
+    };
+    if (active && kv0 <= q0 + 31) {
+      if (kv0 + BKV - 1 > q0) tile(std::true_type());
+      else tile(std::false_type());
+    }
+    __syncthreads();
   }
   if (!active) return;
   store_acc_rows<T, HD>(dqkv + ((long long)b * Tn + q) * ld + h * HD, dq, scale, g);
 }
 
-// bf16: head_dim 32, 64, 128; fp32: 32, 64 (the fp32 path exists for small parity configs).
 template <typename T, typename F>
 gpt_status dispatch_hd(int hd, F&& f) {
   switch (hd) {
@@ -421,9 +573,11 @@ template <typename T>
 gpt_status launch_attn_fwd(const T* qkv, T* out, float* lse2, int B, int Tn, int H, int hd,
                            hipStream_t s) {
   const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
-  dim3 grid(cdiv(Tn, 128), H, B);
+  // 32 queries per wave: two workgroups fit a CU, so one wave's softmax overlaps the other's
+  // MFMAs (measured faster at the d32 shape than 64 queries per wave at one workgroup per CU).
   gpt_status st = dispatch_hd<T>(hd, [&](auto HD) {
-    attn_fwd_kernel<T, decltype(HD)::value><<<grid, ATHREADS, 0, s>>>(qkv, out, lse2, Tn, H, sl2);
+    constexpr int hdv = decltype(HD)::value;
+    attn_fwd_kernel<T, hdv, 1><<<dim3(cdiv(Tn, 128), H, B), ATHREADS, 0, s>>>(qkv, out, lse2, Tn, H, sl2);
   });
   return st != GPT_OK ? st : check_launch("attention fwd");
 }

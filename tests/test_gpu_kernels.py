@@ -148,10 +148,12 @@ def _heads(x, Bn, T, H, hd, blk):
     return x[:, blk * D:(blk + 1) * D].reshape(Bn, T, H, hd).transpose(0, 2, 1, 3)
 
 
-@pytest.mark.parametrize("dtype,hd,T", [(BF, 64, 256), (BF, 128, 192), (BF, 32, 64),
-                                        (F32, 32, 128), (F32, 64, 64)])
-def test_attention_fwd_bwd(dtype, hd, T):
-    Bn, H = 2, 3
+@pytest.mark.parametrize("dtype,hd,T,Bn,H", [(BF, 64, 256, 2, 3), (BF, 128, 192, 2, 3),
+                                              (BF, 32, 64, 2, 3), (F32, 32, 128, 2, 3),
+                                              (F32, 64, 64, 2, 3),
+                                              # >= 512 workgroups: 64 queries per wave
+                                              (BF, 128, 512, 16, 16)])
+def test_attention_fwd_bwd(dtype, hd, T, Bn, H):
     D, N = H * hd, Bn * T
     bf = dtype == BF
     qkv0 = _attn_case(dtype, Bn, T, H, hd, 10)
