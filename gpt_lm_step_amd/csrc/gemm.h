@@ -356,39 +356,61 @@ __global__ __launch_bounds__(THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_
     __builtin_amdgcn_sched_barrier(0);
     const T* As = lds[cur];
     const T* Bs = lds[cur] + BM * C::PITCH;
+    // fragments of the next 16-wide K slice are read while the current slice's MFMAs run
+    vec8_t<T> af[2][TM], bfr[2][TN];
+    auto read = [&](int ks, int slot) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[slot][i] = load8(As + (wm + i * 32 + lr) * C::PITCH + ks + lg * 8);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[slot][j] = load8(Bs + (wn + j * 32 + lr) * C::PITCH + ks + lg * 8);
+    };
+    read(0, 0);
 #pragma unroll
     for (int ks = 0; ks < C::BK; ks += 16) {
-      vec8_t<T> af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = load8(As + (wm + i * 32 + lr) * C::PITCH + ks + lg * 8);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = load8(Bs + (wn + j * 32 + lr) * C::PITCH + ks + lg * 8);
+      const int slot = (ks / 16) & 1;
+      if (ks + 16 < C::BK) read(ks + 16, slot ^ 1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) Mma<T>::run(acc[i][j], bfr[j], af[i]);
+        for (int j = 0; j < TN; ++j) Mma<T>::run(acc[i][j], bfr[slot][j], af[slot][i]);
     }
     __syncthreads();
   }
 
-  // The MFMA computed each 32 x 32 tile transposed (B fragment first), so its output layout
-  // gives lane l output row l%32 and, in registers 4q..4q+3, the four consecutive columns
-  // q*8 + (l/32)*4 + 0..3: the epilogue moves 4 columns per access.
+  // Epilogue through LDS (free once the last K tile is consumed).  The MFMA computed each
+  // 32 x 32 tile transposed (B fragment first), so lane l holds output row l%32 and, in
+  // registers 4q..4q+3, columns q*8 + (l/32)*4 + 0..3.  Each wave writes 32-row slices of its
+  // (BM/2) x (BN/2) tile to its own LDS region (row pitch BN/2 + 4 floats: conflict-free), then
+  // reads them back row-major so that 32 lanes cover 128 consecutive columns of one row: the
+  // epilogue's global accesses are contiguous 256 B (bf16) / 512 B (fp32) row segments.
+  {
+    constexpr int WC = BN / 2, EP = WC + 4;  // wave tile columns, LDS row pitch in floats
+    static_assert(4 * 32 * EP * 4 <= 2 * (BM + BN) * Cfg<T>::PITCH * (int)sizeof(T),
+                  "epilogue staging must fit the operand buffers");
+    float* ep = reinterpret_cast<float*>(&lds[0][0]) + w * 32 * EP;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int row = m0 + wm + i * 32 + lr;
-    if (row >= M) continue;
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = n0 + wn + j * 32 + q * 8 + lg * 4;
-        if (col < N) {
-          const float v[4] = {acc[i][j][q * 4], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2],
-                              acc[i][j][q * 4 + 3]};
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = {acc[i][j][q * 4], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2],
+                           acc[i][j][q * 4 + 3]};
+          *reinterpret_cast<f32x4*>(ep + lr * EP + j * 32 + q * 8 + lg * 4) = v;
+        }
+      // lanes 0..WC/4-1 take consecutive 4-column groups of one row; WAVE*4/WC rows per pass
+      constexpr int LPR = WC / 4, RPP = WAVE / LPR;
+#pragma unroll
+      for (int rr = 0; rr < 32; rr += RPP) {
+        const int r = rr + lane / LPR, c4 = (lane % LPR) * 4;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(ep + r * EP + c4);
+        const int row = m0 + wm + i * 32 + r, col = n0 + wn + c4;
+        if (row < M && col < N) {
+          const float v[4] = {x[0], x[1], x[2], x[3]};
           epi(row, col, v);
         }
       }
+    }
   }
 }
 

@@ -190,33 +190,70 @@ __global__ __launch_bounds__(256) void rms_bwd_kernel(
 }
 
 // ------------------------------------------------------------------ rotary + QK-norm
-// In place on the q and k column blocks of qkv [N, 3D].  One thread per rotation pair
-// (i, i + Hd/2) of one head; the Hd/2 lanes of a head reduce the head's sum of squares.
-// rstd_qk [N, 2H]: q heads then k heads.
+// In place on the q and k column blocks of qkv [N, 3D].  One thread per 4 consecutive rotation
+// pairs (i..i+3, i+half..i+half+3) of one head: 8-byte (bf16) / 16-byte (fp32) accesses; the
+// Hd/8 lanes of a head reduce the head's sum of squares.  rstd_qk [N, 2H]: q heads then k heads.
+template <typename T>
+__device__ __forceinline__ void ld4(const T* p, float (&v)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (float)x[i];
+  } else {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = x[i];
+  }
+}
+template <typename T>
+__device__ __forceinline__ void st4(T* p, const float (&v)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (bf16)v[i];
+    *reinterpret_cast<bf16x4*>(p) = x;
+  } else {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void rope_qknorm_fwd_kernel(
     T* __restrict__ qkv, const T* __restrict__ cos_t, const T* __restrict__ sin_t,
     float* __restrict__ rstd_qk, long long N, int Tn, int H, int hd, int qk_norm, float eps) {
-  const int D = H * hd, half = hd / 2;
+  const int D = H * hd, half = hd / 2, per_tok = D / 4;  // threads per token (q and k)
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= N * D) return;  // D is a multiple of 64: whole waves exit together
-  const long long tok = gid / D;
-  const int p = (int)(gid % D);
+  if (gid >= N * per_tok) return;  // per_tok is a multiple of 16: whole lane groups exit together
+  const long long tok = gid / per_tok;
+  const int p = (int)(gid % per_tok) * 4;
   const int hq = p / half, i = p % half;
   const int t = (int)(tok % Tn);
   T* base = qkv + tok * 3 * D + (hq < H ? 0 : D) + (hq % H) * hd;
-  const float x1 = to_f32(base[i]), x2 = to_f32(base[i + half]);
-  const float c = to_f32(cos_t[t * half + i]), s = to_f32(sin_t[t * half + i]);
-  float y1 = x1 * c + x2 * s;
-  float y2 = -x1 * s + x2 * c;
+  float x1[4], x2[4], c[4], sn[4], y1[4], y2[4];
+  ld4(base + i, x1);
+  ld4(base + i + half, x2);
+  ld4(cos_t + t * half + i, c);
+  ld4(sin_t + t * half + i, sn);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y1[e] = x1[e] * c[e] + x2[e] * sn[e];
+    y2[e] = -x1[e] * sn[e] + x2[e] * c[e];
+    ss += y1[e] * y1[e] + y2[e] * y2[e];
+  }
   float r = 1.f;
   if (qk_norm) {
-    const float ss = group_sum(y1 * y1 + y2 * y2, half);
+    ss = group_sum(ss, half / 4);
     r = 1.f / sqrtf(ss / (float)hd + eps);
     if (i == 0) rstd_qk[tok * 2 * H + hq] = r;
   }
-  base[i] = from_f32<T>(y1 * r);
-  base[i + half] = from_f32<T>(y2 * r);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y1[e] *= r;
+    y2[e] *= r;
+  }
+  st4(base + i, y1);
+  st4(base + i + half, y2);
 }
 
 // Backward on the dq, dk column blocks of dqkv, in place: dz = r (dy - y mean(dy y)) with y
@@ -227,25 +264,41 @@ __global__ __launch_bounds__(256) void rope_qknorm_bwd_kernel(
     T* __restrict__ dqkv, const T* __restrict__ qkv, const T* __restrict__ cos_t,
     const T* __restrict__ sin_t, const float* __restrict__ rstd_qk, long long N, int Tn, int H,
     int hd, int qk_norm) {
-  const int D = H * hd, half = hd / 2;
+  const int D = H * hd, half = hd / 2, per_tok = D / 4;
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= N * D) return;
-  const long long tok = gid / D;
-  const int p = (int)(gid % D);
+  if (gid >= N * per_tok) return;
+  const long long tok = gid / per_tok;
+  const int p = (int)(gid % per_tok) * 4;
   const int hq = p / half, i = p % half;
   const int t = (int)(tok % Tn);
   const long long off = tok * 3 * D + (hq < H ? 0 : D) + (hq % H) * hd;
-  float d1 = to_f32(dqkv[off + i]), d2 = to_f32(dqkv[off + i + half]);
+  float d1[4], d2[4], c[4], sn[4], o1[4], o2[4];
+  ld4(dqkv + off + i, d1);
+  ld4(dqkv + off + i + half, d2);
   if (qk_norm) {
-    const float y1 = to_f32(qkv[off + i]), y2 = to_f32(qkv[off + i + half]);
+    float y1[4], y2[4];
+    ld4(qkv + off + i, y1);
+    ld4(qkv + off + i + half, y2);
     const float r = rstd_qk[tok * 2 * H + hq];
-    const float mean = group_sum(d1 * y1 + d2 * y2, half) / (float)hd;
-    d1 = r * (d1 - y1 * mean);
-    d2 = r * (d2 - y2 * mean);
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dot += d1[e] * y1[e] + d2[e] * y2[e];
+    const float mean = group_sum(dot, half / 4) / (float)hd;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      d1[e] = r * (d1[e] - y1[e] * mean);
+      d2[e] = r * (d2[e] - y2[e] * mean);
+    }
   }
-  const float c = to_f32(cos_t[t * half + i]), s = to_f32(sin_t[t * half + i]);
-  dqkv[off + i] = from_f32<T>(d1 * c - d2 * s);
-  dqkv[off + i + half] = from_f32<T>(d1 * s + d2 * c);
+  ld4(cos_t + t * half + i, c);
+  ld4(sin_t + t * half + i, sn);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o1[e] = d1[e] * c[e] - d2[e] * sn[e];
+    o2[e] = d1[e] * sn[e] + d2[e] * c[e];
+  }
+  st4(dqkv + off + i, o1);
+  st4(dqkv + off + i + half, o2);
 }
 
 // ------------------------------------------------------------------ elementwise helpers
@@ -351,8 +404,8 @@ template <typename T>
 gpt_status launch_rope_qknorm_fwd(T* qkv, const T* cos_t, const T* sin_t, float* rstd_qk,
                                   long long N, int Tn, int H, int hd, int qk_norm, float eps,
                                   hipStream_t s) {
-  rope_qknorm_fwd_kernel<T><<<cdiv(N * H * hd, 256), 256, 0, s>>>(qkv, cos_t, sin_t, rstd_qk, N,
-                                                                  Tn, H, hd, qk_norm, eps);
+  rope_qknorm_fwd_kernel<T><<<cdiv(N * H * hd / 4, 256), 256, 0, s>>>(qkv, cos_t, sin_t, rstd_qk,
+                                                                      N, Tn, H, hd, qk_norm, eps);
   return check_launch("rope+qknorm fwd");
 }
 
@@ -360,8 +413,8 @@ template <typename T>
 gpt_status launch_rope_qknorm_bwd(T* dqkv, const T* qkv, const T* cos_t, const T* sin_t,
                                   const float* rstd_qk, long long N, int Tn, int H, int hd,
                                   int qk_norm, hipStream_t s) {
-  rope_qknorm_bwd_kernel<T><<<cdiv(N * H * hd, 256), 256, 0, s>>>(dqkv, qkv, cos_t, sin_t,
-                                                                  rstd_qk, N, Tn, H, hd, qk_norm);
+  rope_qknorm_bwd_kernel<T><<<cdiv(N * H * hd / 4, 256), 256, 0, s>>>(dqkv, qkv, cos_t, sin_t,
+                                                                      rstd_qk, N, Tn, H, hd, qk_norm);
   return check_launch("rope+qknorm bwd");
 }
 
