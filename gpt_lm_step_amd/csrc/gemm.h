@@ -414,9 +414,196 @@ __global__ __launch_bounds__(THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_
   }
 }
 
+// ---------------------------------------------------------------- bf16: DMA-staged kernel
+// Operand tiles travel global -> LDS by buffer loads that write LDS directly (16 B per lane,
+// 1 KB per wave instruction, lane l to byte 16*l of the instruction's LDS block), in the
+// operand's own global layout, so no staging registers and no LDS store instructions are used:
+//  * K-contiguous tile: [ROWS][64] bf16, 128 B rows, 16 B chunk c of row r at chunk position
+//    c ^ ((r >> 1) & 7) (fragment reads of 16 rows hit 16 distinct bank groups);
+//  * row-contiguous tile: [64 k][ROWS] bf16, chunk c of k-row k at c ^ (4 * (k % 4)); its MFMA
+//    fragments come from two transposing LDS reads (ds_read_b64_tr_b16: within a 16-lane
+//    group, lane j receives element j%4 of lanes j/4 + 4i, i = 0..3; lane 4i + t addresses
+//    row k0 + i, columns n0 + 4t .. +3, so lane j gets B[k0 .. k0+3][n0 + j]).
+// Loads past the operand's end read as zeros (buffer range check).  Two LDS stages: the DMA of
+// tile kt+1 runs during the MFMAs of tile kt and is waited for at the barrier.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int ROWS, bool KC>
+struct DmaTile {
+  static constexpr int BYTES = ROWS * 64 * 2;
+  static constexpr int NI = BYTES / 1024 / 4;           // DMA instructions per wave
+  // issue this wave's DMA instructions for the tile at (row0, k0)
+  static __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, long long ld, int row0,
+                                               int k0, int rows_lim, int k_lim, bf16* tile) {
+    const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int blk = w * NI + i;  // 1 KB block of the tile
+      uint32_t off;
+      if constexpr (KC) {
+        const int r = blk * 8 + lane / 8, c = (lane % 8) ^ ((r >> 1) & 7);
+        const int row = row0 + r, k = k0 + c * 8;
+        off = (row < rows_lim && k < k_lim) ? (uint32_t)(((long long)row * ld + k) * 2) : OOB;
+      } else {
+        constexpr int CPR = ROWS / 8, KPI = 1024 / (ROWS * 2);  // chunks per k-row, k-rows per block
+        const int kk = blk * KPI + lane / CPR, c = (lane % CPR) ^ (4 * (kk % 4));
+        const int row = row0 + c * 8, k = k0 + kk;
+        off = (row < rows_lim && k < k_lim) ? (uint32_t)(((long long)k * ld + row) * 2) : OOB;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(tile + blk * 512), 16, off, 0, 0, 0);
+    }
+  }
+  // 8 consecutive K values (k = ks + g*8 .. +7) of tile row r (r = lane's row)
+  static __device__ __forceinline__ bf16x8 frag(const bf16* tile, int r, int ks, int lane) {
+    const int g = (lane / 32) % 2;
+    if constexpr (KC) {
+      const int c = ks / 8 + g;
+      return load8(tile + r * 64 + ((c ^ ((r >> 1) & 7)) * 8));
+    } else {
+      // r = rowbase + lane % 32; the 16-lane group of this lane covers rows nb .. nb+15
+      const int j = lane % 16, i = j / 4, t = j % 4;
+      const int nb = r - j;
+      bf16x8 v;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = ks + g * 8 + h * 4 + i;
+        const int n = nb + 4 * t;
+        const int pos = (((n / 8) ^ (4 * (k % 4))) * 8) + (n % 8);
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(tile + k * ROWS + pos));
+        const bf16x4 y = __builtin_bit_cast(bf16x4, x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[h * 4 + e] = y[e];
+      }
+      return v;
+    }
+  }
+};
+
+template <int BM, int BN, bool A_KC, bool B_KC, class Epi, int SITE>
+__global__ __launch_bounds__(THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_dma_kernel(
+    const bf16* __restrict__ A, long long lda, const bf16* __restrict__ B, long long ldb, int M,
+    int N, int K, uint32_t a_bytes, uint32_t b_bytes, Epi epi) {
+  constexpr int TM = BM / 64, TN = BN / 64, BK = 64;
+  using TA = DmaTile<BM, A_KC>;
+  using TB = DmaTile<BN, B_KC>;
+  __shared__ __attribute__((aligned(1024))) bf16 lds[2][(BM + BN) * BK];
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE;
+  const int wm = (w / 2) * (BM / 2), wn = (w % 2) * (BN / 2);
+  const int lr = lane % 32, lg = lane / 32;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, a_bytes), rb = make_rsrc(B, b_bytes);
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+
+  const int nk = (K + BK - 1) / BK;
+  TA::issue(ra, lda, m0, 0, M, K, lds[0]);
+  TB::issue(rb, ldb, n0, 0, N, K, lds[0] + BM * BK);
+  __syncthreads();  // waits for this wave's DMA, then all waves'
+
+  // The compiler cannot tell a transposing LDS read from the tile that an LDS-DMA in flight
+  // is writing, so it waits for all outstanding DMA before such a read.  With a row-contiguous
+  // operand every fragment of the tile is therefore read first and the next tile's DMA issued
+  // after; with K-contiguous operands the DMA goes first and the reads of slice s+1 overlap
+  // the MFMAs of slice s.
+  constexpr bool READ_FIRST = !(A_KC && B_KC);
+  constexpr int NS = READ_FIRST ? BK / 16 : 2;  // fragment slots
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bf16* As = lds[cur];
+    const bf16* Bs = lds[cur] + BM * BK;
+    bf16x8 af[NS][TM], bfr[NS][TN];
+    auto read = [&](int ks, int slot) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[slot][i] = TA::frag(As, wm + i * 32 + lr, ks, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[slot][j] = TB::frag(Bs, wn + j * 32 + lr, ks, lane);
+    };
+    auto issue_next = [&]() {
+      if (kt + 1 < nk) {
+        TA::issue(ra, lda, m0, (kt + 1) * BK, M, K, lds[cur ^ 1]);
+        TB::issue(rb, ldb, n0, (kt + 1) * BK, N, K, lds[cur ^ 1] + BM * BK);
+      }
+    };
+    if constexpr (READ_FIRST) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) read(s * 16, s);
+      issue_next();
+    } else {
+      issue_next();
+      read(0, 0);
+    }
+#pragma unroll
+    for (int ks = 0; ks < BK; ks += 16) {
+      const int slot = READ_FIRST ? ks / 16 : (ks / 16) & 1;
+      if (!READ_FIRST && ks + 16 < BK) read(ks + 16, slot ^ 1);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) Mma<bf16>::run(acc[i][j], bfr[slot][j], af[slot][i]);
+    }
+    // keep the barrier (and the DMA wait in front of it) behind the MFMAs, which touch no
+    // memory and would otherwise be scheduled past it
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  }
+
+  // epilogue through LDS, as in gemm_kernel
+  {
+    constexpr int WC = BN / 2, EP = WC + 4;
+    static_assert(4 * 32 * EP * 4 <= 2 * (BM + BN) * BK * 2, "epilogue staging must fit");
+    float* ep = reinterpret_cast<float*>(&lds[0][0]) + w * 32 * EP;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = {acc[i][j][q * 4], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2],
+                           acc[i][j][q * 4 + 3]};
+          *reinterpret_cast<f32x4*>(ep + lr * EP + j * 32 + q * 8 + lg * 4) = v;
+        }
+      constexpr int LPR = WC / 4, RPP = WAVE / LPR;
+#pragma unroll
+      for (int rr = 0; rr < 32; rr += RPP) {
+        const int r = rr + lane / LPR, c4 = (lane % LPR) * 4;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(ep + r * EP + c4);
+        const int row = m0 + wm + i * 32 + r, col = n0 + wn + c4;
+        if (row < M && col < N) {
+          const float v[4] = {x[0], x[1], x[2], x[3]};
+          epi(row, col, v);
+        }
+      }
+    }
+  }
+}
+
 // Bytes spanned by an operand of `rows` x K (KC: rows of ld; RC: K rows of ld).
 inline long long operand_bytes(bool kc, long long rows, long long K, long long ld, long long es) {
   return (kc ? (rows - 1) * ld + K : (K - 1) * ld + rows) * es;
+}
+
+template <int BM, int BN, class Epi, int SITE>
+void launch_dma(bool a_kc, bool b_kc, int M, int N, int K, const bf16* A, long long lda,
+                const bf16* B, long long ldb, const Epi& epi, hipStream_t s) {
+  dim3 grid((unsigned)(cdiv(M, BM) * cdiv(N, BN)));
+  const uint32_t ab = (uint32_t)operand_bytes(a_kc, M, K, lda, 2);
+  const uint32_t bb = (uint32_t)operand_bytes(b_kc, N, K, ldb, 2);
+#define GEMM_DMA(AK, BK_)                                                                       \
+  gemm_dma_kernel<BM, BN, AK, BK_, Epi, SITE><<<grid, THREADS, 0, s>>>(A, lda, B, ldb, M, N, K, \
+                                                                      ab, bb, epi)
+  if (a_kc && b_kc) GEMM_DMA(true, true);
+  else if (a_kc) GEMM_DMA(true, false);
+  else if (b_kc) GEMM_DMA(false, true);
+  else GEMM_DMA(false, false);
+#undef GEMM_DMA
 }
 
 template <typename T, int BM, int BN, class Epi, int SITE>
@@ -460,9 +647,9 @@ inline gpt_status gemm(bool a_kc, bool b_kc, int M, int N, int K, const T* A, lo
   if ((long long)cdiv(M, 128) * cdiv(N, 128) >= (1LL << 31)) return fail(GPT_ESHAPE, "gemm: too many tiles");
   if constexpr (std::is_same<T, bf16>::value) {
     if (big_tiles >= 240)
-      gemm_detail::launch_tiles<T, 256, 256, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
+      gemm_detail::launch_dma<256, 256, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
     else
-      gemm_detail::launch_tiles<T, 128, 128, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
+      gemm_detail::launch_dma<128, 128, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
   } else {
     // fp32 serves the small parity configurations only
     gemm_detail::launch_tiles<T, 64, 64, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
