@@ -66,11 +66,14 @@ def cpu_baseline(cfg, flat_dev, tokens, n_tok):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {a.gpus}",
+        print(f"bench.py measures one GPU only: the step has no multi-GPU path (got --gpus {a.gpus})",
               file=sys.stderr)
         sys.exit(2)
     import torch
     from gpt_lm_step_amd import binding as B
+    if not os.path.exists(B._LIB_PATH):
+        from gpt_lm_step_amd import build
+        build.build()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
