@@ -1,13 +1,17 @@
 #!/usr/bin/env python3
 """Throughput of one decoder training step (forward + hand-written backward) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload d32|gpt2|tiny]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload d32|gpt2|tiny|tables|speedrun]
 
-Prints ONE JSON line: tokens/s of the whole fwd+bwd step (inputs already in HBM), MFU against
-the bf16 dense MFMA peak using the nanochat estimate_flops convention
-(6*(params - embedding) + 12*L*H*Hd*T per token), the roofline of the dominant kernel
-(timed live with HIP events around each launch of an instrumented pass), and the CPU oracle
-timed on a bounded sample of the same workload on this host's cores.
+Prints ONE JSON line.  Dense workloads (d32 default, gpt2, tiny): tokens/s of the whole fwd+bwd
+step (inputs already in HBM), MFU against the bf16 dense MFMA peak using the nanochat
+estimate_flops convention (6*(params - embedding) + 12*L*H*Hd*T per token), the roofline of the
+dominant kernel and of every stage (timed live with HIP events around each launch of an
+instrumented pass), and the CPU oracle timed on a bounded sample of the same workload on this
+host's cores.  `tables`: the hashed-bigram gather and the fused scatter-reduce + per-row update
+of both tables over 196,608 tokens.  `speedrun`: one optimizer step of the GPT-2-small model
+with both bigram tables and the trigram table, 24 accumulated micro-batches of 8 x 1024 tokens,
+then one in-place update per table.
 """
 from __future__ import annotations
 
@@ -25,7 +29,8 @@ PEAK_BF16 = 2.5e15       # MI355X dense bf16 MFMA, FLOP/s
 PEAK_FP32 = 157.3e12     # MI355X fp32 (matrix and vector), FLOP/s
 PEAK_HBM = 8.0e12        # MI355X HBM3E, B/s
 METRIC = "train tokens/sec (fwd+bwd) on 1 MI355X + MFU vs bf16 MFMA peak"
-WORKLOADS = {"d32": configs.D32, "gpt2": configs.GPT2_SMALL, "tiny": configs.TINY}
+DENSE = {"d32": configs.D32, "gpt2": configs.GPT2_SMALL, "tiny": configs.TINY}
+WORKLOADS = sorted(list(DENSE) + ["tables", "speedrun"])
 # Stages made of several kernels (their time is not one kernel's launch duration).
 MULTI_KERNEL = {"wte_segsum"}
 
@@ -35,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="d32", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="d32", choices=WORKLOADS)
     ap.add_argument("--profile-steps", type=int, default=2)
     ap.add_argument("--cpu-tokens", type=int, default=384,
                     help="tokens of the CPU-oracle sample (one sequence)")
@@ -43,19 +48,24 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(cfg, flat_dev, tokens, n_tok):
-    """The oracle (fp64 numpy, as it stands) on one sequence of n_tok tokens of the same model."""
-    import torch
+def _cores():
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(cfg, flat_dev, tokens, n_tok, addends=None):
+    """The oracle (fp64 numpy, as it stands) on one sequence of n_tok tokens of the same model.
+    `addends`: optional callable (tokens [1, n_tok+1]) -> (x0_add, v_add, tri_rows) on the host."""
     from threadpoolctl import threadpool_limits
     from oracle import model as om
-    cores = len(os.sched_getaffinity(0))
+    cores = _cores()
     flat = flat_dev.float().cpu().numpy()
     params = inputs.unflatten(cfg, flat)
     sub = cfg.replace(batch=1, seq_len=n_tok)
     tok = np.ascontiguousarray(tokens[:1, :n_tok + 1])
+    adds = addends(tok) if addends else (None, None, None)
     with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
-        res = om.forward_backward(sub, params, tok)
+        res = om.forward_backward(sub, params, tok, *adds)
         dt = time.perf_counter() - t0
     assert np.isfinite(res.loss)
     return {"value": n_tok / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
@@ -63,21 +73,63 @@ def cpu_baseline(cfg, flat_dev, tokens, n_tok):
                       f"vocab, fp64 numpy fwd+bwd), {dt:.1f} s"}
 
 
-def main():
-    a = parse()
-    if a.gpus != 1:
-        print(f"bench.py measures one GPU only: the step has no multi-GPU path (got --gpus {a.gpus})",
-              file=sys.stderr)
-        sys.exit(2)
+def _roof_entry(name, calls, tot_ms, flops, nbytes, bf16):
+    """Roofline of one stage: algorithmic work per launch / average launch duration."""
+    per_launch_s = tot_ms / calls / 1e3
+    if flops > 0:
+        peak = PEAK_BF16 if bf16 else PEAK_FP32
+        ach = flops / calls / per_launch_s
+        return {"bound": "mfma", "kernel": name, "achieved": round(ach / 1e12, 1),
+                "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                "avg_launch_ms": round(per_launch_s * 1e3, 4), "algorithmic_per_launch": flops / calls}
+    ach = nbytes / calls / per_launch_s
+    return {"bound": "hbm", "kernel": name, "achieved": round(ach / 1e9, 1),
+            "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": round(ach / PEAK_HBM, 4),
+            "avg_launch_ms": round(per_launch_s * 1e3, 4), "algorithmic_per_launch": nbytes / calls}
+
+
+def profile_stages(B, ctx, step, n_steps, bf16):
+    """Instrumented pass: every launch bracketed by events on the step's stream.  Returns the
+    dominant single-kernel stage's roofline and a per-stage table."""
     import torch
-    from gpt_lm_step_amd import binding as B
-    if not os.path.exists(B._LIB_PATH):
-        from gpt_lm_step_amd import build
-        build.build()
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    cfg = WORKLOADS[a.workload]
+    B.gpt_profile(ctx, True)
+    for _ in range(n_steps):
+        step()
+    B.gpt_profile(ctx, False)
+    stages = B.gpt_profile_read(ctx)
+    torch.cuda.synchronize()
+    ps = max(n_steps, 1)
+    parts = {}
+    for n, c, m, f, b in stages:
+        e = _roof_entry(n, c, m, f, b, bf16)
+        parts[n] = {"ms_per_step": round(m / ps, 3), "launches": c // ps,
+                    "achieved": e["achieved"], "unit": e["unit"], "frac": e["frac"]}
+    single = [s for s in stages if s[0] not in MULTI_KERNEL]
+    name, calls, tot_ms, flops, nbytes = max(single, key=lambda s: s[2])
+    roof = _roof_entry(name, calls, tot_ms, flops, nbytes, bf16)
+    roof["traffic"] = None
+    roof["launches_per_step"] = calls // ps
+    return roof, parts
+
+
+def time_steps(step, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, time.perf_counter() - w0
+
+
+def bench_dense(a, B):
+    import torch
+    cfg = DENSE[a.workload]
     seeds = inputs.seeds_for(cfg.name)
     bf16 = cfg.dtype == configs.BF16
     tokens = inputs.step_tokens(cfg, seeds["tokens"], zipf=bf16)
@@ -92,48 +144,10 @@ def main():
     def step():
         B.gpt_fwd_bwd(ctx, t_in, t_tg, params, grads, loss)
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    w0 = time.perf_counter()
-    e0.record()
-    for _ in range(a.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms = e0.elapsed_time(e1) / a.steps
+    ms, wall = time_steps(step, a.steps, a.warmup)
     lval = float(loss.item())
     assert np.isfinite(lval), lval
-
-    # instrumented pass: every launch bracketed by events on the step's stream
-    B.gpt_profile(ctx, True)
-    for _ in range(a.profile_steps):
-        step()
-    B.gpt_profile(ctx, False)
-    stages = B.gpt_profile_read(ctx)
-    torch.cuda.synchronize()
-    ps = max(a.profile_steps, 1)
-    stage_ms = {n: round(m / ps, 3) for n, c, m, f, b in stages}
-    single = [s for s in stages if s[0] not in MULTI_KERNEL]
-    name, calls, tot_ms, flops, nbytes = max(single, key=lambda s: s[2])
-    per_launch_s = tot_ms / calls / 1e3
-    if flops > 0:
-        peak = PEAK_BF16 if bf16 else PEAK_FP32
-        achieved = flops / calls / per_launch_s
-        roof = {"bound": "mfma", "kernel": name, "achieved": round(achieved / 1e12, 1),
-                "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": None, "launches_per_step": calls // ps,
-                "avg_launch_ms": round(per_launch_s * 1e3, 4),
-                "algorithmic_per_launch": flops / calls}
-    else:
-        achieved = nbytes / calls / per_launch_s
-        roof = {"bound": "hbm", "kernel": name, "achieved": round(achieved / 1e9, 1),
-                "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4),
-                "traffic": None, "launches_per_step": calls // ps,
-                "avg_launch_ms": round(per_launch_s * 1e3, 4),
-                "algorithmic_per_launch": nbytes / calls}
+    roof, parts = profile_stages(B, ctx, step, a.profile_steps, bf16)
 
     tok_s = cfg.tokens / (ms / 1e3)
     fpt = configs.flops_per_token(cfg)
@@ -150,10 +164,238 @@ def main():
         "mfu": round(fpt * tok_s / peak, 4),
         "hw_mfu": round(configs.hardware_flops_per_step(cfg) / (ms / 1e3) / peak, 4),
         "flops_per_token": fpt, "loss": round(lval, 5), "wall_s": round(wall, 3),
-        "roofline": roof, "stage_ms_per_step": stage_ms,
+        "roofline": roof, "parts": parts,
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, params, tokens, min(a.cpu_tokens, cfg.seq_len))
+    return out
+
+
+def _tables(tc, seed, tri_seed=None):
+    """Device tables: x0 (2^21 rows) and value (2^20 rows) N(0, 0.02), trigram N(0, 1); bf16."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    tx0 = (torch.randn(tc.x0_rows, tc.dim, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    tv = (torch.randn(tc.v_rows, tc.dim, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    ttri = None
+    if tri_seed is not None:
+        g.manual_seed(tri_seed)
+        ttri = torch.randn(tc.tri_rows, tc.dim, device="cuda", generator=g).to(torch.bfloat16)
+    return tx0, tv, ttri
+
+
+def gather_bytes(n, dim, unique):
+    """Algorithmic bytes of one gather-add: tokens + h (4 B each), each distinct row read once,
+    y read and written (bf16)."""
+    return n * 8 + unique * dim * 2 + 2 * n * dim * 2
+
+
+def update_bytes(n, dim, unique):
+    """Algorithmic bytes of one scatter-reduce + update: h, dy once, each touched row read and
+    written, plus its fp32 second moment read and written."""
+    return n * 4 + n * dim * 2 + unique * (2 * dim * 2 + 8)
+
+
+def _timed(fn, evs):
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn()
+    e1.record()
+    evs.append((e0, e1))
+
+
+def cpu_tables_baseline(tc, n_seq=32, rows_log2=18):
+    """The oracle's hash + gather-add + sparse row update (fp64 numpy, as it stands) on the
+    first n_seq sequences, tables of 2^rows_log2 rows (the oracle copies whole tables in fp64)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import tables as ot
+    cores = _cores()
+    seeds = inputs.seeds_for("tables")
+    tok = inputs.zipf_tokens(seeds["tokens"], (tc.n_tokens // tc.seq_len, tc.seq_len), tc.vocab)[:n_seq]
+    R = 1 << rows_log2
+    table = inputs.normal(seeds["weights"], (R, tc.dim), 0.02, True)
+    dy = inputs.normal(seeds["dy"], (tok.size, tc.dim), 1.0, True)
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        h = ot.hash_indices(tok, 2, tc.vocab, R)
+        y = ot.gather_add(np.zeros((tok.size, tc.dim), np.float32), table, h)
+        ot.sparse_row_update(table, np.zeros(R), h, dy, tc.lr, tc.beta2, tc.eps)
+        dt = time.perf_counter() - t0
+    assert np.isfinite(y).all()
+    return {"value": tok.size / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_seq} sequences x {tc.seq_len} tokens, one table of 2^{rows_log2} x "
+                      f"{tc.dim} rows: hash + gather-add + sparse update in fp64 numpy, {dt:.1f} s"}
+
+
+def bench_tables(a, B):
+    import torch
+    tc = configs.TABLES
+    seeds = inputs.seeds_for("tables")
+    n_seq = tc.n_tokens // tc.seq_len
+    tok = torch.from_numpy(inputs.zipf_tokens(seeds["tokens"], (n_seq, tc.seq_len), tc.vocab)).cuda()
+    N, D = tc.n_tokens, tc.dim
+    tx0, tv, _ = _tables(tc, seeds["weights"])
+    g = torch.Generator(device="cuda").manual_seed(seeds["dy"])
+    dy = torch.randn(N, D, device="cuda", generator=g).to(torch.bfloat16)
+    v_x0 = torch.zeros(tc.x0_rows, device="cuda")
+    v_v = torch.zeros(tc.v_rows, device="cuda")
+    y_x0 = torch.zeros(N, D, device="cuda", dtype=torch.bfloat16)
+    y_v = torch.zeros(N, D, device="cuda", dtype=torch.bfloat16)
+    h_x0 = torch.empty(N, device="cuda", dtype=torch.int32)
+    h_v = torch.empty(N, device="cuda", dtype=torch.int32)
+    ws = torch.empty(max(B.bigram_workspace_bytes(N, D, tc.x0_rows),
+                         B.bigram_workspace_bytes(N, D, tc.v_rows)), dtype=torch.uint8, device="cuda")
+    parts = [("gather_x0", lambda: B.bigram_fwd(tok, 2, tc.vocab, tx0, y_x0, h_x0)),
+             ("gather_v", lambda: B.bigram_fwd(tok, 2, tc.vocab, tv, y_v, h_v)),
+             ("update_x0", lambda: B.bigram_bwd_update(h_x0, dy, tx0, v_x0, tc.lr, tc.beta2, tc.eps, ws)),
+             ("update_v", lambda: B.bigram_bwd_update(h_v, dy, tv, v_v, tc.lr, tc.beta2, tc.eps, ws))]
+
+    def step():
+        for _, fn in parts:
+            fn()
+
+    ms, wall = time_steps(step, a.steps, a.warmup)
+    # per-part event timing over the same number of steps
+    evs = {n: [] for n, _ in parts}
+    for _ in range(a.steps):
+        for n, fn in parts:
+            _timed(fn, evs[n])
+    torch.cuda.synchronize()
+    part_ms = {n: sum(e0.elapsed_time(e1) for e0, e1 in v) / len(v) for n, v in evs.items()}
+    u_x0 = int(torch.unique(h_x0).numel())
+    u_v = int(torch.unique(h_v).numel())
+    seg = torch.unique(h_x0, return_counts=True)[1]
+    edges = [1, 4, 16, 64, 256, 1 << 62]
+    hist = {(f"{lo}-{hi - 1}" if hi < edges[-1] else f">={lo}"): int(((seg >= lo) & (seg < hi)).sum())
+            for lo, hi in zip(edges[:-1], edges[1:])}
+    alg = {"gather_x0": gather_bytes(N, D, u_x0), "gather_v": gather_bytes(N, D, u_v),
+           "update_x0": update_bytes(N, D, u_x0), "update_v": update_bytes(N, D, u_v)}
+    table = {}
+    for n in part_ms:
+        gbs = alg[n] / (part_ms[n] / 1e3) / 1e9
+        table[n] = {"ms": round(part_ms[n], 4), "algorithmic_bytes": alg[n],
+                    "achieved": round(gbs, 1), "unit": "GB/s", "frac": round(gbs * 1e9 / PEAK_HBM, 4)}
+    dom = "gather_x0"  # one kernel per call: its launch duration is the call's
+    roof = {"bound": "hbm", "kernel": "bigram_fwd (hash + gather-add, x0 table)",
+            "achieved": table[dom]["achieved"], "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+            "frac": table[dom]["frac"], "traffic": None, "launches_per_step": 1,
+            "avg_launch_ms": table[dom]["ms"], "algorithmic_per_launch": alg[dom]}
+    out = {
+        "metric": "hashed-table tokens/sec (gather fwd + scatter-reduce/update bwd, 2 tables) on 1 MI355X",
+        "value": round(N / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Zipf(1.1) tokens, N(0,0.02) tables, N(0,1) upstream grads)",
+        "config": {"workload": "hashed bigram tables: x0 2^21x768 + value 2^20x768 bf16, 196608 tokens",
+                   "tokens": N, "dim": D, "x0_rows": tc.x0_rows, "v_rows": tc.v_rows,
+                   "unique_rows_x0": u_x0, "unique_rows_v": u_v, "largest_segment": int(seg.max()),
+                   "segment_hist_x0": hist, "parallelism": "none (1 GPU)"},
+        "wall_s": round(wall, 3), "roofline": roof, "parts": table,
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_tables_baseline(tc)
+    return out
+
+
+def bench_speedrun(a, B):
+    import torch
+    cfg = configs.SPEEDRUN
+    tc = configs.TABLES
+    MB = configs.SPEEDRUN_MICRO_BATCHES
+    seeds = inputs.seeds_for(cfg.name)
+    T, N, D, V = cfg.seq_len, cfg.tokens, cfg.d_model, cfg.vocab
+    tokens = inputs.zipf_tokens(seeds["tokens"], (MB * cfg.batch, T + 1), V)
+    t_in = torch.from_numpy(np.ascontiguousarray(tokens[:, :T])).cuda().view(MB, cfg.batch, T)
+    t_tg = torch.from_numpy(np.ascontiguousarray(tokens[:, 1:])).cuda().view(MB, cfg.batch, T)
+    params = inputs.device_params(cfg, seeds["weights"])
+    grads = torch.empty(configs.param_elems(cfg), device="cuda")
+    loss = torch.zeros(1, device="cuda")
+    ctx = B.gpt_init(cfg)
+    tx0, tv, ttri = _tables(tc, seeds["tables"], seeds["trigram"])
+    v_x0 = torch.zeros(tc.x0_rows, device="cuda")
+    v_v = torch.zeros(tc.v_rows, device="cuda")
+    bf = torch.bfloat16
+    add_x0 = torch.empty(N, D, device="cuda", dtype=bf)
+    add_v = torch.empty(N, D, device="cuda", dtype=bf)
+    add_tri = torch.empty(N, D, device="cuda", dtype=bf)
+    d_x0 = torch.empty(MB * N, D, device="cuda", dtype=bf)   # per-token addend grads, staged
+    d_v = torch.empty(MB * N, D, device="cuda", dtype=bf)
+    h_x0 = torch.empty(MB * N, device="cuda", dtype=torch.int32)
+    h_v = torch.empty(MB * N, device="cuda", dtype=torch.int32)
+    ws = torch.empty(max(B.bigram_workspace_bytes(MB * N, D, tc.x0_rows),
+                         B.bigram_workspace_bytes(MB * N, D, tc.v_rows)), dtype=torch.uint8, device="cuda")
+
+    def step():
+        for i in range(MB):
+            sl = slice(i * N, (i + 1) * N)
+            add_x0.zero_()
+            add_v.zero_()
+            add_tri.zero_()
+            B.bigram_fwd(t_in[i], 2, V, tx0, add_x0, h_x0[sl])
+            B.bigram_fwd(t_in[i], 2, V, tv, add_v, h_v[sl])
+            B.bigram_fwd(t_in[i], 3, V, ttri, add_tri)
+            B.gpt_fwd_bwd(ctx, t_in[i], t_tg[i], params, grads, loss, 1.0 / MB, int(i > 0),
+                          add_x0, add_v, add_tri, d_x0[sl], d_v[sl])
+        B.bigram_bwd_update(h_x0, d_x0, tx0, v_x0, tc.lr, tc.beta2, tc.eps, ws)
+        B.bigram_bwd_update(h_v, d_v, tv, v_v, tc.lr, tc.beta2, tc.eps, ws)
+
+    ms, wall = time_steps(step, a.steps, a.warmup)
+    lval = float(loss.item())
+    assert np.isfinite(lval), lval
+    # stages of the dense micro-batch step
+    roof, parts = profile_stages(B, ctx, lambda: B.gpt_fwd_bwd(
+        ctx, t_in[0], t_tg[0], params, grads, loss, 1.0 / MB, 1, add_x0, add_v, add_tri,
+        d_x0[:N], d_v[:N]), a.profile_steps, True)
+    n_tok = MB * N
+    tok_s = n_tok / (ms / 1e3)
+    fpt = configs.flops_per_token(cfg)
+    out = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Zipf tokens, N(0,0.02) weights and tables, N(0,1) trigram rows)",
+        "config": {"workload": "speedrun-shaped optimizer step: gpt2-small + x0/value bigram "
+                               "tables + frozen trigram, 24 x 8 x 1024 tokens",
+                   "micro_batches": MB, "tokens_per_step": n_tok, "layers": cfg.n_layer,
+                   "d_model": D, "vocab": V, "parallelism": "none (1 GPU)"},
+        "mfu": round(fpt * tok_s / PEAK_BF16, 4), "flops_per_token": fpt,
+        "loss_last_micro_batch": round(lval, 5), "wall_s": round(wall, 3),
+        "roofline": roof, "parts_micro_batch": parts,
+    }
+    if not a.no_cpu_baseline:
+        from oracle import tables as ot
+
+        def addends(tok):
+            rows = []
+            for table, order, R in ((tx0, 2, tc.x0_rows), (tv, 2, tc.v_rows), (ttri, 3, tc.tri_rows)):
+                h = ot.hash_indices(tok[:, :-1], order, V, R).reshape(-1)
+                rows.append(table[torch.from_numpy(h).cuda()].float().cpu().numpy())
+            return tuple(rows)
+        out["cpu_baseline"] = cpu_baseline(cfg, params, tokens, min(a.cpu_tokens, T), addends)
+    return out
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only: the step has no multi-GPU path (got --gpus {a.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from gpt_lm_step_amd import binding as B
+    if not os.path.exists(B._LIB_PATH):
+        from gpt_lm_step_amd import build
+        build.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if a.workload == "tables":
+        out = bench_tables(a, B)
+    elif a.workload == "speedrun":
+        out = bench_speedrun(a, B)
+    else:
+        out = bench_dense(a, B)
     print(json.dumps(out), flush=True)
 
 
