@@ -1,17 +1,18 @@
 // Hashed n-gram tables on gfx950: hash + gather-add, and the table backward with the sparse
-// per-row optimizer inlined (decoder-rtx posts by Chris McCormick, baseline-4 thread: bigram
-// tables added to x0 and to values, "sparse, no first moment, and only per-row magnitude",
-// no .grad buffers).  The same sort + segmented reduction also produces the dense embedding
-// gradient (a deterministic scatter-add without float atomics).
+// per-row optimizer inlined (ChrisJMcCormick post feed, the posts on the hashed bigram tables
+// added to x0 and to the attention values: the table optimizer keeps no momentum and one
+// magnitude statistic per row, and no gradient buffer exists).  The same sort + segmented
+// reduction also produces the dense embedding gradient (a deterministic scatter-add without
+// float atomics).
 //
 // Backward pipeline for n per-token gradient rows keyed by table row:
 //   1. stable LSD radix sort of (key, token) pairs, 8-bit digits, keys outside the table
-//      mapped to a sentinel that sorts last;
-//   2. run boundaries -> segment starts (one segment per distinct row);
-//   3. each segment is cut into chunks of SEG_CHUNK tokens; one wavefront sums one chunk in
-//      ascending token order;
-//   4. single-chunk segments finalize at once; longer ones write fp32 partials that a second
-//      kernel adds in chunk order before finalizing.
+//      mapped to a sentinel that sorts last: per pass a tile histogram and a scatter that
+//      scans the histogram for its own offsets;
+//   2. one wavefront per tile of SEG_TILE sorted positions sums the runs of equal keys it
+//      holds in ascending sorted (= token) order and finalizes the rows that lie inside it;
+//   3. rows crossing tile edges leave fp32 partials that a second kernel adds in tile order
+//      before finalizing.
 // Summation order is fixed, so results are bitwise reproducible run to run.
 #include "kernels.h"
 
@@ -21,7 +22,7 @@ namespace {
 
 constexpr int SCAN_THREADS = 256, SCAN_ITEMS = 8, SCAN_TILE = SCAN_THREADS * SCAN_ITEMS;
 constexpr int RS_THREADS = 256, RS_ROUNDS = 8, RS_TILE = RS_THREADS * RS_ROUNDS;
-constexpr int SEG_CHUNK = 32;
+constexpr int SEG_TILE = 64;  // sorted positions per wavefront in the segmented sums
 constexpr uint64_t HASH_MULT = 1000003ull;
 
 // ------------------------------------------------------------------ hash + gather
@@ -89,135 +90,82 @@ __device__ __forceinline__ int block_excl_scan(int x, int* smem /* >= 16 */, int
   return before + inc - x;
 }
 
-struct ItemArray {
-  const int* a;
-  long long n;
-  __device__ int operator()(long long i) const { return i < n ? a[i] : 0; }
-};
-// 1 at the first element of every run of equal sorted keys.
-struct ItemRunHead {
-  const uint32_t* k;
-  long long n;
-  __device__ int operator()(long long i) const {
-    return i < n && (i == 0 || k[i] != k[i - 1]) ? 1 : 0;
-  }
-};
-// Chunks of segment u (0 for u >= number of segments).
-struct ItemChunks {
-  const int* seg_start;
-  const int* n_seg;
-  __device__ int operator()(long long u) const {
-    if (u >= *n_seg) return 0;
-    int len = seg_start[u + 1] - seg_start[u];
-    return (len + SEG_CHUNK - 1) / SEG_CHUNK;
-  }
-};
-// Partial slots of segment u: its chunk count when it has more than one chunk.
-struct ItemPartials {
-  const int* chunk_base;
-  const int* n_seg;
-  __device__ int operator()(long long u) const {
-    if (u >= *n_seg) return 0;
-    int c = chunk_base[u + 1] - chunk_base[u];
-    return c > 1 ? c : 0;
-  }
-};
-
-template <class Item>
-__global__ void scan_tile_sums(Item item, long long n, int* bsum) {
-  __shared__ int smem[16];
-  const long long base = (long long)blockIdx.x * SCAN_TILE + threadIdx.x * SCAN_ITEMS;
-  int s = 0;
-#pragma unroll
-  for (int i = 0; i < SCAN_ITEMS; ++i) s += item(base + i);
-  int total;
-  block_excl_scan(s, smem, &total);
-  if (threadIdx.x == 0) bsum[blockIdx.x] = total;
-}
-
-__global__ void scan_block_sums(int* bsum, int nb, int* total_out) {
-  __shared__ int smem[16];
-  const int per = (nb + blockDim.x - 1) / blockDim.x;
-  const int b0 = threadIdx.x * per;
-  int s = 0;
-  for (int i = 0; i < per; ++i)
-    if (b0 + i < nb) s += bsum[b0 + i];
-  int total;
-  int run = block_excl_scan(s, smem, &total);
-  for (int i = 0; i < per; ++i)
-    if (b0 + i < nb) {
-      int v = bsum[b0 + i];
-      bsum[b0 + i] = run;
-      run += v;
-    }
-  if (threadIdx.x == 0 && total_out) *total_out = total;
-}
-
-template <class Item>
-__global__ void scan_apply(Item item, long long n, const int* bsum, int* out) {
-  __shared__ int smem[16];
-  const long long base = (long long)blockIdx.x * SCAN_TILE + threadIdx.x * SCAN_ITEMS;
-  int v[SCAN_ITEMS], s = 0;
-#pragma unroll
-  for (int i = 0; i < SCAN_ITEMS; ++i) {
-    v[i] = item(base + i);
-    s += v[i];
-  }
-  int total;
-  int run = block_excl_scan(s, smem, &total) + bsum[blockIdx.x];
-#pragma unroll
-  for (int i = 0; i < SCAN_ITEMS; ++i) {
-    if (base + i < n) out[base + i] = run;
-    run += v[i];
-  }
-}
-
-struct ScanScratch {
-  int* bsum;  // cdiv(n, SCAN_TILE) ints
-};
-
-template <class Item>
-void excl_scan(Item item, long long n, int* out, int* total, int* bsum, hipStream_t s) {
-  const unsigned nb = cdiv(n, SCAN_TILE);
-  scan_tile_sums<<<nb, SCAN_THREADS, 0, s>>>(item, n, bsum);
-  scan_block_sums<<<1, 1024, 0, s>>>(bsum, (int)nb, total);
-  scan_apply<<<nb, SCAN_THREADS, 0, s>>>(item, n, bsum, out);
-}
-
 // ------------------------------------------------------------------ radix sort
-__global__ void sort_init(const int32_t* __restrict__ h, long long n, long long rows,
-                          uint32_t* __restrict__ keys, uint32_t* __restrict__ vals) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const int32_t k = h[i];
-  keys[i] = (k >= 0 && k < rows) ? (uint32_t)k : (uint32_t)rows;  // sentinel sorts last
-  vals[i] = (uint32_t)i;
+constexpr int INLINE_OFFS_TILES = 256;  // up to this many tiles the scatter finds its own offsets
+
+__device__ __forceinline__ uint32_t clamp_key(int32_t k, long long rows) {
+  return (k >= 0 && k < rows) ? (uint32_t)k : (uint32_t)rows;  // sentinel sorts last
 }
 
-__global__ void radix_hist(const uint32_t* __restrict__ keys, long long n, int shift, int nblk,
-                           int* __restrict__ hist /* [256][nblk] */) {
+// hist[d][blk] = number of keys of tile blk (current order) whose digit at `shift` is d.  The
+// first pass reads the keys straight from h.
+__global__ void radix_hist(const int32_t* __restrict__ h, const uint32_t* __restrict__ keys,
+                           long long n, long long rows, int shift, int nblk,
+                           int* __restrict__ hist) {
   __shared__ int cnt[256];
   cnt[threadIdx.x] = 0;
   __syncthreads();
   const long long base = (long long)blockIdx.x * RS_TILE;
 #pragma unroll
   for (int r = 0; r < RS_ROUNDS; ++r) {
-    long long i = base + r * RS_THREADS + threadIdx.x;
-    if (i < n) atomicAdd(&cnt[(keys[i] >> shift) & 255u], 1);
+    const long long i = base + r * RS_THREADS + threadIdx.x;
+    if (i < n) {
+      const uint32_t k = h ? clamp_key(h[i], rows) : keys[i];
+      atomicAdd(&cnt[(k >> shift) & 255u], 1);
+    }
   }
   __syncthreads();
-  hist[threadIdx.x * nblk + blockIdx.x] = cnt[threadIdx.x];
+  hist[(long long)threadIdx.x * nblk + blockIdx.x] = cnt[threadIdx.x];
 }
 
-// Stable scatter: items of a tile are ranked in index order, round by round; inside a round
-// lanes with equal digits are matched with 8 ballots.
-__global__ void radix_scatter(const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin,
+// Scatter offset of digit d in tile blk: all keys of smaller digits plus digit d's keys in
+// earlier tiles (exclusive scan of hist in [digit][tile] order).
+__device__ __forceinline__ int digit_offset(const int* __restrict__ hist, int nblk, int* smem) {
+  const int d = threadIdx.x;
+  const int* row = hist + (long long)d * nblk;
+  int before = 0, total = 0;
+#pragma unroll 8
+  for (int b = 0; b < nblk; ++b) {
+    const int c = row[b];
+    total += c;
+    before += (b < (int)blockIdx.x) ? c : 0;
+  }
+  int all;
+  return block_excl_scan(total, smem, &all) + before;
+}
+
+// Offsets for many tiles: the same scan by one workgroup, written to hist in place.
+__global__ __launch_bounds__(1024) void radix_offsets(int* __restrict__ a, int nblk) {
+  __shared__ int smem[16];
+  const long long m = 256LL * nblk;
+  const long long per = (m + blockDim.x - 1) / blockDim.x;
+  const long long b0 = (long long)threadIdx.x * per;
+  int s = 0;
+  for (long long i = 0; i < per; ++i)
+    if (b0 + i < m) s += a[b0 + i];
+  int total;
+  int run = block_excl_scan(s, smem, &total);
+  for (long long i = 0; i < per; ++i)
+    if (b0 + i < m) {
+      const int v = a[b0 + i];
+      a[b0 + i] = run;
+      run += v;
+    }
+}
+
+// Stable scatter of one digit: items of a tile are ranked in index order, round by round;
+// inside a round lanes with equal digits are matched with 8 ballots.  The first pass reads
+// the keys from h (clamped) with values = token index.  `scanned`: hist already holds offsets.
+__global__ void radix_scatter(const int32_t* __restrict__ h, long long rows,
+                              const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin,
                               uint32_t* __restrict__ kout, uint32_t* __restrict__ vout,
-                              long long n, int shift, int nblk, const int* __restrict__ offs) {
+                              long long n, int shift, int nblk, const int* __restrict__ hist,
+                              int scanned) {
   __shared__ int base[256];
   __shared__ int wcnt[RS_THREADS / WAVE][256];
+  __shared__ int smem[16];
   const int tid = threadIdx.x, lane = tid % WAVE, w = tid / WAVE;
-  base[tid] = offs[tid * nblk + blockIdx.x];
+  base[tid] = scanned ? hist[(long long)tid * nblk + blockIdx.x] : digit_offset(hist, nblk, smem);
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int r = 0; r < RS_ROUNDS; ++r) {
 #pragma unroll
@@ -227,8 +175,13 @@ __global__ void radix_scatter(const uint32_t* __restrict__ kin, const uint32_t* 
     const bool valid = i < n;
     uint32_t k = 0, v = 0, d = 0;
     if (valid) {
-      k = kin[i];
-      v = vin[i];
+      if (h) {
+        k = clamp_key(h[i], rows);
+        v = (uint32_t)i;
+      } else {
+        k = kin[i];
+        v = vin[i];
+      }
       d = (k >> shift) & 255u;
     }
     uint64_t mask = __ballot(valid);
@@ -256,22 +209,7 @@ __global__ void radix_scatter(const uint32_t* __restrict__ kin, const uint32_t* 
   }
 }
 
-// ------------------------------------------------------------------ segments
-__global__ void seg_scatter_starts(const uint32_t* __restrict__ k, long long n,
-                                   const int* __restrict__ pos, const int* __restrict__ n_seg,
-                                   int* __restrict__ seg_start) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n && (i == 0 || k[i] != k[i - 1])) seg_start[pos[i]] = (int)i;
-  if (i == 0) seg_start[*n_seg] = (int)n;
-}
-
-__global__ void chunk_list(const int* __restrict__ chunk_base, const int* __restrict__ n_seg,
-                           int* __restrict__ chunk_seg) {
-  const long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (u >= *n_seg) return;
-  for (int c = chunk_base[u]; c < chunk_base[u + 1]; ++c) chunk_seg[c] = (int)u;
-}
-
+// ------------------------------------------------------------------ per-row sums + finish
 enum { MODE_UPDATE = 0, MODE_GRAD = 1 };
 
 template <typename T>
@@ -283,164 +221,378 @@ struct Finish {
   int beta;
 };
 
-// acc[gi][e] holds columns (lane + 64*gi)*8 + e of the row sum g.
-template <typename T, int MODE, int MAXG>
-__device__ __forceinline__ void finish_row(const Finish<T>& f, uint32_t row, int dim,
-                                           float (&acc)[MAXG][8]) {
-  const int lane = threadIdx.x % WAVE, groups = dim / 8;
-  if (MODE == MODE_GRAD) {
+// Rows are moved through a buffer resource over the one row (its base is wave-uniform), lane l
+// owning the 4-element groups q = l + 64*gi (gi < G), columns 4q .. 4q+3.  Lanes past the row's
+// end get an offset beyond the resource: their loads read zeros and their stores are dropped,
+// so no load or store sits behind a per-lane branch.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t ROW_OOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), (short)0, bytes, 0x00020000);
+}
+
+// Raw words of four elements (bf16: two dwords, fp32: four) and their float values.
+template <typename S> struct Raw4;
+template <> struct Raw4<bf16> {
+  typedef u32x2 type;
+  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(rs, off * 2, 0, 0);
+  }
+  static __device__ __forceinline__ void cvt(type v, float (&o)[4]) {
+    o[0] = __uint_as_float(v[0] << 16);
+    o[1] = __uint_as_float(v[0] & 0xffff0000u);
+    o[2] = __uint_as_float(v[1] << 16);
+    o[3] = __uint_as_float(v[1] & 0xffff0000u);
+  }
+};
+template <> struct Raw4<float> {
+  typedef u32x4 type;
+  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, off * 4, 0, 0);
+  }
+  static __device__ __forceinline__ void cvt(type v, float (&o)[4]) {
 #pragma unroll
-    for (int gi = 0; gi < MAXG; ++gi) {
-      const int g = lane + gi * WAVE;
-      if (g < groups) {
-        float* o = f.out + (size_t)row * dim + g * 8;
-        float r[8];
-        if (f.beta) {
-          f32x8 old = *reinterpret_cast<const f32x8*>(o);
+    for (int e = 0; e < 4; ++e) o[e] = __uint_as_float(v[e]);
+  }
+};
+template <typename S>
+__device__ __forceinline__ void ld4(__amdgpu_buffer_rsrc_t rs, uint32_t off, const S*, float (&o)[4]) {
+  Raw4<S>::cvt(Raw4<S>::load(rs, off), o);
+}
+__device__ __forceinline__ void st4(__amdgpu_buffer_rsrc_t rs, uint32_t off, bf16*, const float (&o)[4]) {
+  bf16x4 b;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) r[e] = old[e] + acc[gi][e];
-        } else {
+  for (int e = 0; e < 4; ++e) b[e] = (bf16)o[e];
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), rs, off * 2, 0, 0);
+}
+__device__ __forceinline__ void st4(__amdgpu_buffer_rsrc_t rs, uint32_t off, float*, const float (&o)[4]) {
+  const u32x4 v = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                   __float_as_uint(o[3])};
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, off * 4, 0, 0);
+}
+
+template <int G>
+__device__ __forceinline__ void zero_acc(float (&a)[G][4]) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) r[e] = acc[gi][e];
-        }
-        store8_f32(o, r);
-      }
+  for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[gi][e] = 0.f;
+}
+
+// element offset of lane's group gi, or past the end (elements; scaled to bytes in ld4/st4)
+__device__ __forceinline__ uint32_t group_off(int gi, int dim) {
+  const int q = threadIdx.x % WAVE + gi * WAVE;
+  return q * 4 < dim ? (uint32_t)(q * 4) : ROW_OOB / 4;
+}
+
+// live == false (wave-uniform): every lane reads zeros.
+template <int G, typename S>
+__device__ __forceinline__ void load_row(const S* p, int dim, float (&x)[G][4], bool live = true) {
+  const __amdgpu_buffer_rsrc_t rs = row_rsrc(p, dim * (int)sizeof(S));
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) ld4(rs, live ? group_off(gi, dim) : ROW_OOB / 4, p, x[gi]);
+}
+
+template <int G, typename S>
+__device__ __forceinline__ void store_row(S* p, int dim, const float (&x)[G][4]) {
+  const __amdgpu_buffer_rsrc_t rs = row_rsrc(p, dim * (int)sizeof(S));
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) st4(rs, group_off(gi, dim), p, x[gi]);
+}
+
+// What the row's finish reads, fetched before the sums so that both latencies overlap (kept as
+// raw words until the finish, so nothing waits for them earlier).
+template <typename T, int MODE, int G>
+struct FinishIn {
+  using S = typename std::conditional<MODE == MODE_UPDATE, T, float>::type;
+  typename Raw4<S>::type raw[G];  // MODE_UPDATE: table row; MODE_GRAD: old output row
+  float v;                        // MODE_UPDATE: second moment of the row
+  bool have;                      // MODE_GRAD: beta = 1 (old output row loaded)
+  __device__ __forceinline__ void fetch(const Finish<T>& f, uint32_t row, int dim) {
+    const S* p;
+    if constexpr (MODE == MODE_UPDATE) {
+      v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(row_rsrc(f.v + row, 4), 0, 0, 0));
+      p = f.table + (size_t)row * dim;
+      have = true;
+    } else {
+      v = 0.f;
+      p = f.out + (size_t)row * dim;
+      have = f.beta != 0;
     }
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(p, dim * (int)sizeof(S));
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) raw[gi] = Raw4<S>::load(rs, have ? group_off(gi, dim) : ROW_OOB / 4);
+  }
+  __device__ __forceinline__ void values(float (&w)[G][4]) const {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) Raw4<S>::cvt(raw[gi], w[gi]);
+  }
+};
+
+// MODE_UPDATE: v = beta2 v + (1 - beta2) mean(g^2); w -= lr g / (sqrt(v) + eps).
+// MODE_GRAD: out = (beta ? out : 0) + g.
+template <typename T, int MODE, int G>
+__device__ __forceinline__ void finish_row(const Finish<T>& f, uint32_t row, int dim,
+                                           const float (&acc)[G][4], const FinishIn<T, MODE, G>& in) {
+  float w[G][4];
+  in.values(w);
+  if constexpr (MODE == MODE_GRAD) {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[gi][e] += acc[gi][e];
+    store_row<G>(f.out + (size_t)row * dim, dim, w);
   } else {
     float ss = 0.f;
 #pragma unroll
-    for (int gi = 0; gi < MAXG; ++gi)
+    for (int gi = 0; gi < G; ++gi)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss += acc[gi][e] * acc[gi][e];
+      for (int e = 0; e < 4; ++e) ss += acc[gi][e] * acc[gi][e];
     ss = wave_sum(ss);
-    const float vr = f.beta2 * f.v[row] + (1.f - f.beta2) * (ss / (float)dim);
+    const float vr = f.beta2 * in.v + (1.f - f.beta2) * (ss / (float)dim);
     const float step = f.lr / (sqrtf(vr) + f.eps);
-    if (lane == 0) f.v[row] = vr;
 #pragma unroll
-    for (int gi = 0; gi < MAXG; ++gi) {
-      const int g = lane + gi * WAVE;
-      if (g < groups) {
-        T* p = f.table + (size_t)row * dim + g * 8;
-        float w[8];
-        load8_f32(p, w);
+    for (int gi = 0; gi < G; ++gi)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] -= step * acc[gi][e];
-        store8_f32(p, w);
-      }
-    }
+      for (int e = 0; e < 4; ++e) w[gi][e] -= step * acc[gi][e];
+    store_row<G>(f.table + (size_t)row * dim, dim, w);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(vr), row_rsrc(f.v + row, 4),
+                                          threadIdx.x % WAVE == 0 ? 0u : ROW_OOB, 0, 0);
   }
 }
 
-template <typename T, typename DyT, int MODE, int MAXG>
-__global__ __launch_bounds__(256) void seg_chunk_kernel(
+// Rows in flight per wave while summing (register budget: U * G * 4 floats).
+template <int G> constexpr int unroll_rows() { return G <= 1 ? 8 : (G <= 2 ? 4 : 2); }
+
+constexpr uint32_t NO_KEY = 0xffffffffu;  // above every key (keys <= rows < 2^31)
+
+// Sum of the gradient rows of sorted positions [j, pe) of the tile (token ids in `tok`,
+// lane-indexed), in ascending order with U rows in flight.  Slots past pe load zeros, which
+// leave the sum unchanged, so the U loads of a round are issued back to back.
+template <int G, int U, typename DyT>
+__device__ __forceinline__ void sum_rows(const DyT* __restrict__ dy, int dim, uint32_t tok, int j,
+                                         int pe, float (&acc)[G][4]) {
+  zero_acc<G>(acc);
+  for (int j0 = j; j0 < pe; j0 += U) {
+    float x[U][G][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t t = (uint32_t)__builtin_amdgcn_readlane((int)tok, min(j0 + u, pe - 1));
+      load_row<G>(dy + t * dim, dim, x[u], j0 + u < pe);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[gi][q] += x[u][gi][q];
+  }
+}
+
+// A run of equal keys inside one tile ("piece"): sorted positions [j, pe) of the tile.
+struct Piece {
+  int j, pe;
+  uint32_t row;
+  bool live, starts, ends;  // live: row inside the table
+};
+
+// Loads of one piece, issued ahead of the previous piece's stores and kept as raw words: the
+// finish operands and the first U gradient rows.  A piece that is not live loads zeros.
+template <typename T, typename DyT, int MODE, int G, int U>
+struct PieceLoads {
+  FinishIn<T, MODE, G> in;
+  typename Raw4<DyT>::type x[U][G];
+  __device__ __forceinline__ void issue(const Piece& p, const DyT* __restrict__ dy, int dim,
+                                        uint32_t tok, const Finish<T>& fin) {
+    in.fetch(fin, p.live ? p.row : 0u, dim);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool on = p.live && p.j + u < p.pe;
+      const size_t t = (uint32_t)__builtin_amdgcn_readlane((int)tok, min(p.j + u, p.pe - 1));
+      const DyT* r = dy + t * dim;
+      const __amdgpu_buffer_rsrc_t rs = row_rsrc(r, dim * (int)sizeof(DyT));
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) x[u][gi] = Raw4<DyT>::load(rs, on ? group_off(gi, dim) : ROW_OOB / 4);
+    }
+  }
+  // the piece's gradient sum: the rows in flight, then (long pieces) the rest
+  __device__ __forceinline__ void sum(const Piece& p, const DyT* __restrict__ dy, int dim,
+                                      uint32_t tok, float (&acc)[G][4]) const {
+    zero_acc<G>(acc);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        float x4[4];
+        Raw4<DyT>::cvt(x[u][gi], x4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[gi][q] += x4[q];
+      }
+    if (p.j + U < p.pe) {
+      float rest[G][4];
+      sum_rows<G, U>(dy, dim, tok, p.j + U, p.pe, rest);
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[gi][q] += rest[gi][q];
+    }
+  }
+};
+
+// One wavefront per tile of SEG_TILE sorted positions: keys and token ids arrive in one load
+// each, the pieces come from one ballot, and each piece's gradient rows are summed in sorted
+// (= token) order.  Only a tile's first piece (continuing a row from earlier tiles) and last
+// piece (a row that goes on) can be incomplete: their sums go to partial slots 2*tile and
+// 2*tile + 1.  Keys past the table (the sentinel) form a suffix and are skipped.  The complete
+// pieces are finished in a loop whose every pass issues the loads of the next piece, stores
+// the current one and then consumes the next piece's loads, so no load wait covers a store.
+template <typename T, typename DyT, int MODE, int G>
+__global__ __launch_bounds__(256) void seg_tile_kernel(
     const uint32_t* __restrict__ skeys, const uint32_t* __restrict__ svals,
-    const DyT* __restrict__ dy, int dim, long long rows, const int* __restrict__ seg_start,
-    const int* __restrict__ chunk_base, const int* __restrict__ chunk_seg,
-    const int* __restrict__ n_chunks, const int* __restrict__ pbase, float* __restrict__ partial,
-    Finish<T> fin) {
-  const int lane = threadIdx.x % WAVE, groups = dim / 8;
+    const DyT* __restrict__ dy, long long n, int dim, long long rows,
+    float* __restrict__ partial, Finish<T> fin) {
+  constexpr int U = unroll_rows<G>();
+  const int lane = threadIdx.x % WAVE;
   const int wpb = blockDim.x / WAVE;
-  const int total = *n_chunks;
-  for (int c = blockIdx.x * wpb + threadIdx.x / WAVE; c < total; c += gridDim.x * wpb) {
-    const int u = chunk_seg[c];
-    const int s0 = seg_start[u], s1 = seg_start[u + 1];
-    const uint32_t row = skeys[s0];
-    if (row >= rows) continue;  // out-of-range keys (sentinel) are skipped
-    const int nch = chunk_base[u + 1] - chunk_base[u];
-    const int j = c - chunk_base[u];
-    const int a = s0 + j * SEG_CHUNK, b = min(a + SEG_CHUNK, s1);
-    float acc[MAXG][8];
-#pragma unroll
-    for (int gi = 0; gi < MAXG; ++gi)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[gi][e] = 0.f;
-    for (int i = a; i < b; ++i) {
-      const size_t t = svals[i];
-#pragma unroll
-      for (int gi = 0; gi < MAXG; ++gi) {
-        const int g = lane + gi * WAVE;
-        if (g < groups) {
-          float x[8];
-          load8_f32(dy + t * dim + g * 8, x);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[gi][e] += x[e];
-        }
+  const long long ntiles = (n + SEG_TILE - 1) / SEG_TILE;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+  for (long long tile = (long long)blockIdx.x * wpb + wave; tile < ntiles;
+       tile += (long long)gridDim.x * wpb) {
+    const long long P = tile * SEG_TILE;
+    const int len = (int)min<long long>(SEG_TILE, n - P);
+    const uint32_t key = lane < len ? skeys[P + lane] : NO_KEY;
+    const uint32_t tok = lane < len ? svals[P + lane] : 0u;
+    const uint32_t prevkey = P > 0 ? skeys[P - 1] : NO_KEY;
+    const uint32_t nextkey = P + SEG_TILE < n ? skeys[P + SEG_TILE] : NO_KEY;
+    const uint32_t left = __shfl_up(key, 1, WAVE);
+    const uint64_t heads = __ballot(lane < len && (lane == 0 || key != left));
+    const uint64_t dead = __ballot(lane < len && key >= rows);
+    const int lim = dead ? (int)__builtin_ctzll(dead) : len;  // live positions [0, lim)
+    auto piece_at = [&](int j) {
+      Piece p;
+      const uint64_t later = (j + 1 < WAVE) ? (heads & (~0ull << (j + 1))) : 0ull;
+      p.j = j;
+      p.pe = min(later ? (int)__builtin_ctzll(later) : len, lim);
+      p.row = (uint32_t)__builtin_amdgcn_readlane((int)key, min(j, WAVE - 1));
+      p.live = j < lim;
+      p.starts = j > 0 || prevkey != p.row;
+      p.ends = p.pe < len || nextkey != p.row;
+      return p;
+    };
+    auto to_partial = [&](const Piece& p, long long slot) {
+      float acc[G][4];
+      sum_rows<G, U>(dy, dim, tok, p.j, p.pe, acc);
+      store_row<G>(partial + (size_t)slot * dim, dim, acc);
+    };
+    if (lim == 0) continue;
+    int a = 0, b = lim;  // the complete pieces cover positions [a, b)
+    {
+      const Piece p = piece_at(0);
+      if (!p.starts) {
+        to_partial(p, 2 * tile);
+        a = p.pe;
       }
     }
-    if (nch == 1) {
-      finish_row<T, MODE, MAXG>(fin, row, dim, acc);
-    } else {
-      float* p = partial + (size_t)(pbase[u] + j) * dim;
-#pragma unroll
-      for (int gi = 0; gi < MAXG; ++gi) {
-        const int g = lane + gi * WAVE;
-        if (g < groups) store8_f32(p + g * 8, acc[gi]);
+    if (a < b && lim == len) {
+      const int jl = 63 - (int)__builtin_clzll(heads);
+      const Piece p = piece_at(jl);
+      if (!p.ends && jl >= a) {
+        to_partial(p, 2 * tile + 1);
+        b = jl;
       }
+    }
+    if (a >= b) continue;
+    auto clip = [&](Piece p) {
+      p.pe = min(p.pe, b);
+      p.live = p.j < b;
+      return p;
+    };
+    Piece cur = clip(piece_at(a));
+    PieceLoads<T, DyT, MODE, G, U> ld;
+    ld.issue(cur, dy, dim, tok, fin);
+    float acc[G][4];
+    ld.sum(cur, dy, dim, tok, acc);
+    FinishIn<T, MODE, G> in = ld.in;
+    while (true) {
+      // past the last piece the next one is not live: it loads and sums zeros
+      const Piece nxt = clip(piece_at(min(cur.pe, WAVE - 1)));
+      ld.issue(nxt, dy, dim, tok, fin);
+      __builtin_amdgcn_sched_barrier(0);  // the next piece's loads stay ahead of these stores
+      finish_row<T, MODE, G>(fin, cur.row, dim, acc, in);
+      __builtin_amdgcn_sched_barrier(0);
+      const bool last = cur.pe >= b;
+      cur = nxt;
+      ld.sum(cur, dy, dim, tok, acc);
+      in = ld.in;
+      if (last) break;
     }
   }
 }
 
-template <typename T, int MODE, int MAXG>
-__global__ __launch_bounds__(256) void seg_finish_kernel(
-    const uint32_t* __restrict__ skeys, int dim, long long rows,
-    const int* __restrict__ seg_start, const int* __restrict__ chunk_base,
-    const int* __restrict__ n_seg, const int* __restrict__ pbase,
+// One wavefront per row that starts in a tile and goes on past it (found at that tile): adds
+// the row's first partial and then the partials of the following tiles, which begin with the
+// row, in tile order.  Their first keys are read 64 tiles at a time.
+template <typename T, int MODE, int G>
+__global__ __launch_bounds__(256) void seg_tile_finish_kernel(
+    const uint32_t* __restrict__ skeys, long long n, int dim, long long rows,
     const float* __restrict__ partial, Finish<T> fin) {
-  const int lane = threadIdx.x % WAVE, groups = dim / 8;
+  constexpr int U = G <= 4 ? 8 : 4;  // partial rows in flight
+  const int lane = threadIdx.x % WAVE;
   const int wpb = blockDim.x / WAVE;
-  const int total = *n_seg;
-  for (int u = blockIdx.x * wpb + threadIdx.x / WAVE; u < total; u += gridDim.x * wpb) {
-    const int nch = chunk_base[u + 1] - chunk_base[u];
-    if (nch <= 1) continue;
-    const uint32_t row = skeys[seg_start[u]];
-    if (row >= rows) continue;
-    float acc[MAXG][8];
+  const long long ntiles = (n + SEG_TILE - 1) / SEG_TILE;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+  for (long long tile = (long long)blockIdx.x * wpb + wave; tile + 1 < ntiles;
+       tile += (long long)gridDim.x * wpb) {
+    const long long P = tile * SEG_TILE;  // not the last tile: all SEG_TILE positions exist
+    const uint32_t row = skeys[P + SEG_TILE - 1];
+    if (row >= rows || skeys[P + SEG_TILE] != row) continue;         // last piece ends here
+    if (skeys[P] == row && P > 0 && skeys[P - 1] == row) continue;    // the row began earlier
+    FinishIn<T, MODE, G> in;
+    in.fetch(fin, row, dim);
+    float acc[G][4];
+    load_row<G>(partial + (size_t)(2 * tile + 1) * dim, dim, acc);
+    for (long long t0 = tile + 1;; t0 += WAVE) {
+      const long long t = t0 + lane;
+      const bool cont = t < ntiles && skeys[t * SEG_TILE] == row;  // a prefix of the lanes
+      const int cnt = __popcll(__ballot(cont));
+      for (int j0 = 0; j0 < cnt; j0 += U) {
+        float x[U][G][4];
 #pragma unroll
-    for (int gi = 0; gi < MAXG; ++gi)
+        for (int u = 0; u < U; ++u)
+          load_row<G>(partial + (size_t)(2 * (t0 + min(j0 + u, cnt - 1))) * dim, dim, x[u],
+                      j0 + u < cnt);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[gi][e] = 0.f;
-    for (int j = 0; j < nch; ++j) {
-      const float* p = partial + (size_t)(pbase[u] + j) * dim;
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int gi = 0; gi < MAXG; ++gi) {
-        const int g = lane + gi * WAVE;
-        if (g < groups) {
-          float x[8];
-          load8_f32(p + g * 8, x);
+          for (int gi = 0; gi < G; ++gi)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[gi][e] += x[e];
-        }
+            for (int q = 0; q < 4; ++q) acc[gi][q] += x[u][gi][q];
       }
+      if (cnt < WAVE) break;
     }
-    finish_row<T, MODE, MAXG>(fin, row, dim, acc);
+    finish_row<T, MODE, G>(fin, row, dim, acc, in);
   }
 }
 
 // Workspace carve for n keys of width dim.
 struct SegWs {
   uint32_t *k0, *k1, *v0, *v1;
-  int *hist, *bsum, *pos, *seg_start, *chunk_base, *chunk_seg, *pbase, *counters;
+  int* hist;
   float* partial;
 };
 
 SegWs carve_seg(Carver& c, long long n, int dim) {
   SegWs w;
   const long long nblk = cdiv(n, RS_TILE);
-  const long long max_chunks = n + n / SEG_CHUNK + 1;
-  const long long max_partials = 2 * (n / SEG_CHUNK) + 2;
+  const long long ntiles = (n + SEG_TILE - 1) / SEG_TILE;
   w.k0 = c.take<uint32_t>(n);
   w.k1 = c.take<uint32_t>(n);
   w.v0 = c.take<uint32_t>(n);
   w.v1 = c.take<uint32_t>(n);
   w.hist = c.take<int>(256 * nblk);
-  w.bsum = c.take<int>(cdiv(std::max<long long>(256 * nblk, n + 1), SCAN_TILE) + 1);
-  w.pos = c.take<int>(std::max<long long>(256 * nblk, n + 1));
-  w.seg_start = c.take<int>(n + 2);
-  w.chunk_base = c.take<int>(n + 2);
-  w.chunk_seg = c.take<int>(max_chunks);
-  w.pbase = c.take<int>(n + 2);
-  w.counters = c.take<int>(8);
-  w.partial = c.take<float>((size_t)max_partials * dim);
+  w.partial = c.take<float>((size_t)(2 * ntiles) * dim);
   return w;
 }
 
@@ -451,45 +603,41 @@ gpt_status segsum_run(const int32_t* keys, const DyT* dy, long long n, int dim, 
   Carver c(ws, ws_bytes);
   SegWs w = carve_seg(c, n, dim);
   if (!c.ok) return fail(GPT_EWORKSPACE, "segment workspace too small");
-  int* n_seg = w.counters + 0;
-  int* n_chunks = w.counters + 1;
-  int* n_partials = w.counters + 2;
   const int nblk = (int)cdiv(n, RS_TILE);
+  const bool inline_offs = nblk <= INLINE_OFFS_TILES;
 
-  sort_init<<<cdiv(n, 256), 256, 0, s>>>(keys, n, rows, w.k0, w.v0);
   int bits = 1;
   while (bits < 32 && ((uint64_t)rows >> bits) != 0) ++bits;  // sentinel `rows` must fit
-  uint32_t *ki = w.k0, *vi = w.v0, *ko = w.k1, *vo = w.v1;
-  for (int shift = 0; shift < bits; shift += 8) {
-    radix_hist<<<nblk, RS_THREADS, 0, s>>>(ki, n, shift, nblk, w.hist);
-    excl_scan(ItemArray{w.hist, 256LL * nblk}, 256LL * nblk, w.pos, nullptr, w.bsum, s);
-    radix_scatter<<<nblk, RS_THREADS, 0, s>>>(ki, vi, ko, vo, n, shift, nblk, w.pos);
-    std::swap(ki, ko);
-    std::swap(vi, vo);
+  const int passes = (bits + 7) / 8;
+  uint32_t *ki = nullptr, *vi = nullptr, *ko = w.k0, *vo = w.v0;
+  for (int p = 0; p < passes; ++p) {
+    const int32_t* hk = p == 0 ? keys : nullptr;
+    radix_hist<<<nblk, RS_THREADS, 0, s>>>(hk, ki, n, rows, 8 * p, nblk, w.hist);
+    if (!inline_offs) radix_offsets<<<1, 1024, 0, s>>>(w.hist, nblk);
+    radix_scatter<<<nblk, RS_THREADS, 0, s>>>(hk, rows, ki, vi, ko, vo, n, 8 * p, nblk, w.hist,
+                                              inline_offs ? 0 : 1);
+    ki = ko;
+    vi = vo;
+    ko = (ko == w.k0) ? w.k1 : w.k0;
+    vo = (vo == w.v0) ? w.v1 : w.v0;
   }
-  // segments
-  excl_scan(ItemRunHead{ki, n}, n, w.pos, n_seg, w.bsum, s);
-  seg_scatter_starts<<<cdiv(n, 256), 256, 0, s>>>(ki, n, w.pos, n_seg, w.seg_start);
-  excl_scan(ItemChunks{w.seg_start, n_seg}, n + 1, w.chunk_base, n_chunks, w.bsum, s);
-  chunk_list<<<cdiv(n, 256), 256, 0, s>>>(w.chunk_base, n_seg, w.chunk_seg);
-  excl_scan(ItemPartials{w.chunk_base, n_seg}, n + 1, w.pbase, n_partials, w.bsum, s);
 
-  const unsigned grid = (unsigned)std::min<long long>(cdiv(n, 4), 8192);
-  const int maxg = (dim / 8 + WAVE - 1) / WAVE;
-#define SEG_LAUNCH(G)                                                                          \
-  do {                                                                                         \
-    seg_chunk_kernel<T, DyT, MODE, G><<<grid, 256, 0, s>>>(ki, vi, dy, dim, rows, w.seg_start, \
-                                                           w.chunk_base, w.chunk_seg, n_chunks, \
-                                                           w.pbase, w.partial, fin);           \
-    seg_finish_kernel<T, MODE, G><<<grid, 256, 0, s>>>(ki, dim, rows, w.seg_start,              \
-                                                       w.chunk_base, n_seg, w.pbase,            \
-                                                       w.partial, fin);                         \
+  const long long ntiles = (n + SEG_TILE - 1) / SEG_TILE;
+  const unsigned grid = (unsigned)std::min<long long>(cdiv(ntiles, 4), 16384);
+  const int g4 = (dim / 4 + WAVE - 1) / WAVE;
+#define SEG_LAUNCH(G)                                                                           \
+  do {                                                                                          \
+    seg_tile_kernel<T, DyT, MODE, G><<<grid, 256, 0, s>>>(ki, vi, dy, n, dim, rows, w.partial,  \
+                                                          fin);                                 \
+    seg_tile_finish_kernel<T, MODE, G><<<grid, 256, 0, s>>>(ki, n, dim, rows, w.partial, fin);  \
   } while (0)
-  switch (maxg) {
+  switch (g4) {
     case 1: SEG_LAUNCH(1); break;
     case 2: SEG_LAUNCH(2); break;
     case 3: SEG_LAUNCH(3); break;
     case 4: SEG_LAUNCH(4); break;
+    case 5: case 6: SEG_LAUNCH(6); break;
+    case 7: case 8: SEG_LAUNCH(8); break;
     default: return fail(GPT_ESHAPE, "row width above 2048 is not supported");
   }
 #undef SEG_LAUNCH
