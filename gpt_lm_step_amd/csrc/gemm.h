@@ -429,16 +429,18 @@ __global__ __launch_bounds__(THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int ROWS, bool KC>
+template <int ROWS, bool KC, int NW>
 struct DmaTile {
   static constexpr int BYTES = ROWS * 64 * 2;
-  static constexpr int NI = BYTES / 1024 / 4;           // DMA instructions per wave
-  // issue this wave's DMA instructions for the tile at (row0, k0)
+  static constexpr int NI = BYTES / 1024 / NW;          // DMA instructions per wave (NW waves)
+  static_assert(NI * NW * 1024 == BYTES, "tile must split evenly over the waves");
+  // issue this wave's DMA instructions [i0, i1) for the tile at (row0, k0)
   static __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, long long ld, int row0,
-                                               int k0, int rows_lim, int k_lim, bf16* tile) {
+                                               int k0, int rows_lim, int k_lim, bf16* tile,
+                                               int i0 = 0, int i1 = NI) {
     const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
+    for (int i = i0; i < i1; ++i) {
       const int blk = w * NI + i;  // 1 KB block of the tile
       uint32_t off;
       if constexpr (KC) {
@@ -481,20 +483,26 @@ struct DmaTile {
   }
 };
 
-template <int BM, int BN, bool A_KC, bool B_KC, class Epi, int SITE>
-__global__ __launch_bounds__(THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_dma_kernel(
+// BM x BN tile per workgroup of WGM x WGN waves; each wave computes (BM/WGM) x (BN/WGN) as
+// 32 x 32 MFMA tiles.  The 256 x 256 tile runs 8 waves, two per SIMD, so that one wave's MFMAs
+// cover the other's wait for its DMA at the barrier (with one wave per SIMD the operand
+// transfers and the MFMAs do not overlap); the 128 x 128 tile runs 4 waves, two workgroups
+// per CU.
+template <int BM, int BN, int WGM, int WGN, bool A_KC, bool B_KC, class Epi, int SITE>
+__global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_dma_kernel(
     const bf16* __restrict__ A, long long lda, const bf16* __restrict__ B, long long ldb, int M,
     int N, int K, uint32_t a_bytes, uint32_t b_bytes, Epi epi) {
-  constexpr int TM = BM / 64, TN = BN / 64, BK = 64;
-  using TA = DmaTile<BM, A_KC>;
-  using TB = DmaTile<BN, B_KC>;
+  constexpr int NW = WGM * WGN, WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TM = WTM / 32, TN = WTN / 32, BK = 64;
+  using TA = DmaTile<BM, A_KC, NW>;
+  using TB = DmaTile<BN, B_KC, NW>;
   __shared__ __attribute__((aligned(1024))) bf16 lds[2][(BM + BN) * BK];
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE;
-  const int wm = (w / 2) * (BM / 2), wn = (w % 2) * (BN / 2);
+  const int wm = (w / WGN) * WTM, wn = (w % WGN) * WTN;
   const int lr = lane % 32, lg = lane / 32;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, a_bytes), rb = make_rsrc(B, b_bytes);
   f32x16 acc[TM][TN];
@@ -509,45 +517,51 @@ __global__ __launch_bounds__(THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_
   __syncthreads();  // waits for this wave's DMA, then all waves'
 
   // The compiler cannot tell a transposing LDS read from the tile that an LDS-DMA in flight
-  // is writing, so it waits for all outstanding DMA before such a read.  With a row-contiguous
-  // operand every fragment of the tile is therefore read first and the next tile's DMA issued
-  // after; with K-contiguous operands the DMA goes first and the reads of slice s+1 overlap
-  // the MFMAs of slice s.
-  constexpr bool READ_FIRST = !(A_KC && B_KC);
-  constexpr int NS = READ_FIRST ? BK / 16 : 2;  // fragment slots
+  // is writing, so it waits for all outstanding DMA before such a read.  A row-contiguous
+  // operand's fragments are therefore all read before the next tile's DMA is issued; a
+  // K-contiguous operand's fragments are read slice by slice, those of slice s+1 during the
+  // MFMAs of slice s.
+  constexpr bool AF = !A_KC, BF = !B_KC;                   // operands read whole, first
+  constexpr int NSA = AF ? BK / 16 : 2, NSB = BF ? BK / 16 : 2;  // fragment slots
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     const bf16* As = lds[cur];
     const bf16* Bs = lds[cur] + BM * BK;
-    bf16x8 af[NS][TM], bfr[NS][TN];
-    auto read = [&](int ks, int slot) {
+    bf16x8 af[NSA][TM], bfr[NSB][TN];
+    auto read_a = [&](int ks, int slot) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) af[slot][i] = TA::frag(As, wm + i * 32 + lr, ks, lane);
+    };
+    auto read_b = [&](int ks, int slot) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) bfr[slot][j] = TB::frag(Bs, wn + j * 32 + lr, ks, lane);
     };
+    // Branch-free: after the last tile the offsets fall outside K and the DMA writes zeros into
+    // the idle buffer, which nothing reads again before the final barrier.
     auto issue_next = [&]() {
-      if (kt + 1 < nk) {
-        TA::issue(ra, lda, m0, (kt + 1) * BK, M, K, lds[cur ^ 1]);
-        TB::issue(rb, ldb, n0, (kt + 1) * BK, N, K, lds[cur ^ 1] + BM * BK);
-      }
+      TA::issue(ra, lda, m0, (kt + 1) * BK, M, K, lds[cur ^ 1]);
+      TB::issue(rb, ldb, n0, (kt + 1) * BK, N, K, lds[cur ^ 1] + BM * BK);
     };
-    if constexpr (READ_FIRST) {
+    if constexpr (AF) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) read(s * 16, s);
-      issue_next();
-    } else {
-      issue_next();
-      read(0, 0);
+      for (int s = 0; s < NSA; ++s) read_a(s * 16, s);
     }
+    if constexpr (BF) {
+#pragma unroll
+      for (int s = 0; s < NSB; ++s) read_b(s * 16, s);
+    }
+    issue_next();
+    if constexpr (!AF) read_a(0, 0);
+    if constexpr (!BF) read_b(0, 0);
 #pragma unroll
     for (int ks = 0; ks < BK; ks += 16) {
-      const int slot = READ_FIRST ? ks / 16 : (ks / 16) & 1;
-      if (!READ_FIRST && ks + 16 < BK) read(ks + 16, slot ^ 1);
+      const int sa = AF ? ks / 16 : (ks / 16) & 1, sb = BF ? ks / 16 : (ks / 16) & 1;
+      if (!AF && ks + 16 < BK) read_a(ks + 16, sa ^ 1);
+      if (!BF && ks + 16 < BK) read_b(ks + 16, sb ^ 1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) Mma<bf16>::run(acc[i][j], bfr[slot][j], af[slot][i]);
+        for (int j = 0; j < TN; ++j) Mma<bf16>::run(acc[i][j], bfr[sb][j], af[sa][i]);
     }
     // keep the barrier (and the DMA wait in front of it) behind the MFMAs, which touch no
     // memory and would otherwise be scheduled past it
@@ -555,10 +569,14 @@ __global__ __launch_bounds__(THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_
     __syncthreads();
   }
 
-  // epilogue through LDS, as in gemm_kernel
+  // Epilogue through LDS (free once the last K tile is consumed).  The MFMA computed each
+  // 32 x 32 tile transposed (B fragment first), so lane l holds output row l%32 and, in
+  // registers 4q..4q+3, columns q*8 + (l/32)*4 + 0..3.  Each wave writes 32-row slices of its
+  // tile to its own LDS region (row pitch WTN + 4 floats: conflict-free), then reads them back
+  // row-major so that consecutive lanes cover consecutive 4-column groups of one row.
   {
-    constexpr int WC = BN / 2, EP = WC + 4;
-    static_assert(4 * 32 * EP * 4 <= 2 * (BM + BN) * BK * 2, "epilogue staging must fit");
+    constexpr int EP = WTN + 4;
+    static_assert(NW * 32 * EP * 4 <= 2 * (BM + BN) * BK * 2, "epilogue staging must fit");
     float* ep = reinterpret_cast<float*>(&lds[0][0]) + w * 32 * EP;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -570,7 +588,7 @@ __global__ __launch_bounds__(THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_
                            acc[i][j][q * 4 + 3]};
           *reinterpret_cast<f32x4*>(ep + lr * EP + j * 32 + q * 8 + lg * 4) = v;
         }
-      constexpr int LPR = WC / 4, RPP = WAVE / LPR;
+      constexpr int LPR = WTN / 4, RPP = WAVE / LPR;
 #pragma unroll
       for (int rr = 0; rr < 32; rr += RPP) {
         const int r = rr + lane / LPR, c4 = (lane % LPR) * 4;
@@ -590,15 +608,15 @@ inline long long operand_bytes(bool kc, long long rows, long long K, long long l
   return (kc ? (rows - 1) * ld + K : (K - 1) * ld + rows) * es;
 }
 
-template <int BM, int BN, class Epi, int SITE>
+template <int BM, int BN, int WGM, int WGN, class Epi, int SITE>
 void launch_dma(bool a_kc, bool b_kc, int M, int N, int K, const bf16* A, long long lda,
                 const bf16* B, long long ldb, const Epi& epi, hipStream_t s) {
   dim3 grid((unsigned)(cdiv(M, BM) * cdiv(N, BN)));
   const uint32_t ab = (uint32_t)operand_bytes(a_kc, M, K, lda, 2);
   const uint32_t bb = (uint32_t)operand_bytes(b_kc, N, K, ldb, 2);
-#define GEMM_DMA(AK, BK_)                                                                       \
-  gemm_dma_kernel<BM, BN, AK, BK_, Epi, SITE><<<grid, THREADS, 0, s>>>(A, lda, B, ldb, M, N, K, \
-                                                                      ab, bb, epi)
+#define GEMM_DMA(AK, BK_)                                                                      \
+  gemm_dma_kernel<BM, BN, WGM, WGN, AK, BK_, Epi, SITE><<<grid, 64 * WGM * WGN, 0, s>>>(        \
+      A, lda, B, ldb, M, N, K, ab, bb, epi)
   if (a_kc && b_kc) GEMM_DMA(true, true);
   else if (a_kc) GEMM_DMA(true, false);
   else if (b_kc) GEMM_DMA(false, true);
@@ -647,9 +665,9 @@ inline gpt_status gemm(bool a_kc, bool b_kc, int M, int N, int K, const T* A, lo
   if ((long long)cdiv(M, 128) * cdiv(N, 128) >= (1LL << 31)) return fail(GPT_ESHAPE, "gemm: too many tiles");
   if constexpr (std::is_same<T, bf16>::value) {
     if (big_tiles >= 240)
-      gemm_detail::launch_dma<256, 256, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
+      gemm_detail::launch_dma<256, 256, 2, 4, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
     else
-      gemm_detail::launch_dma<128, 128, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
+      gemm_detail::launch_dma<128, 128, 2, 2, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
   } else {
     // fp32 serves the small parity configurations only
     gemm_detail::launch_tiles<T, 64, 64, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
