@@ -75,6 +75,63 @@ __device__ __forceinline__ vec8_t<T> acc_frag(const f32x16& acc, int h) {
   return v;
 }
 
+// bf16 tiles live in LDS as unpadded [rows][HD] with 16-byte chunk c of row r at chunk position
+// c ^ swz(r).  Fragments of a row tile are read as rows (8 consecutive columns of one row) or
+// transposed with ds_read_b64_tr_b16, so no transposed copies are stored.  The swizzle keeps the
+// row reads, the transposing reads and the tile stores free of LDS bank conflicts (checked for
+// 32 and 64 banks of 4 bytes; head dim 64 leaves a 2-way conflict in the 64-bank model).
+template <int HD>
+__device__ __forceinline__ int swz(int r) { return ((10 * r) ^ r) & (HD / 8 - 1); }
+// The swizzle of a row depends only on the row mod 16, and every fragment starts at a row that is
+// a multiple of 16, so each lane's element offsets inside a 16-row band are computed once:
+// row fragments (lane row l%32, column chunk 2c + g) and transposing fragments (see frag_tr).
+template <int HD>
+struct SwOffsets {
+  // row fragment c: rbase + 16 * (c ^ rx); transposing half `part` at d0 = 32 dt:
+  // tbase[part] + 32 * (dt ^ tx[part])   (chunk index bits split as (2c + g) and (4 dt + low))
+  int rbase, rx, tbase[2], tx[2];
+  __device__ __forceinline__ void init(int lane) {
+    const int lr = lane % 32, g = lane / 32;
+    const int sr = swz<HD>(lr);
+    rx = sr >> 1;
+    rbase = lr * HD + 8 * (g ^ (sr & 1));
+    const int j = lane % 16, i = j / 4, t = j % 4;
+    const int low = 2 * (lr / 16) + t / 2;  // chunk bits below 4 dt
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+      const int rl = part * 8 + g * 4 + i;  // row inside the 16-row band
+      const int st = swz<HD>(rl);
+      tx[part] = st >> 2;
+      tbase[part] = rl * HD + 8 * ((low ^ st) & 3) + 4 * (t % 2);
+    }
+  }
+  __device__ __forceinline__ int row(int c) const { return rbase + 16 * (c ^ rx); }
+  __device__ __forceinline__ int tr(int part, int dt) const { return tbase[part] + 32 * (dt ^ tx[part]); }
+};
+// 8 consecutive columns 16c + 8g .. of row r0 + l%32 (r0 a multiple of 16)
+template <int HD>
+__device__ __forceinline__ bf16x8 frag_row_sw(const bf16* lds, const SwOffsets<HD>& so, int r0, int c) {
+  return load8(lds + r0 * HD + so.row(c));
+}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// The transposed operand with the accumulator K permutation (as frag_split on a transposed tile):
+// lane (l%32, g = l/32) gets rows kb + g*4 + 0..3 and kb + 8 + g*4 + 0..3 of column 32 dt + l%32
+// (kb a multiple of 16).  Within a 16-lane group, source lane 4i + t addresses row base + i,
+// columns n0 + 4t .. +3, and output lane j receives rows base + 0..3 of column n0 + j.
+template <int HD>
+__device__ __forceinline__ bf16x8 frag_tr_sw(const bf16* lds, const SwOffsets<HD>& so, int kb, int dt) {
+  bf16x8 v;
+#pragma unroll
+  for (int part = 0; part < 2; ++part) {
+    const bf16* p = lds + kb * HD + so.tr(part, dt);
+    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+    const bf16x4 y = __builtin_bit_cast(bf16x4, x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[part * 4 + e] = y[e];
+  }
+  return v;
+}
+
 // 2^x with the hardware instruction (v_exp_f32; results below 2^-126 flush to 0, 2^-inf = 0).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -132,6 +189,15 @@ struct Tile88 {
 #pragma unroll
     for (int k = 0; k < 8; ++k) store8(lds + (rb * 8 + k) * pitch + cb * 8, r[k]);
   }
+  // bf16: unpadded swizzled row tile (see swz)
+  __device__ __forceinline__ void store_rows_sw(T* lds) const {
+    if (!active) return;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int row = rb * 8 + k;
+      store8(lds + row * HD + ((cb ^ swz<HD>(row)) * 8), r[k]);
+    }
+  }
   __device__ __forceinline__ void store_trans(T* lds, int pitch) const {
     if (!active) return;
 #pragma unroll
@@ -140,6 +206,32 @@ struct Tile88 {
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[k] = r[k][d];
       store8(lds + (cb * 8 + d) * pitch + rb * 8, o);
+    }
+  }
+};
+
+// bf16: one R x HD tile moved global -> registers -> swizzled LDS rows by NT threads, each
+// moving R*HD/(8*NT) chunks of 16 bytes; consecutive threads take consecutive chunks of a row
+// (coalesced loads; each half-row store covers 128 contiguous bytes: no bank conflicts).
+template <typename T, int R, int HD, int NT>
+struct RowStage {
+  static constexpr int CH = HD / 8, PER = R * CH / NT;
+  static_assert(PER * NT == R * CH, "tile must split evenly over the threads");
+  vec8_t<T> r[PER];
+  int t;
+  __device__ __forceinline__ void init(int tt) { t = tt; }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, long long ld, int row0, int lim) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = t + i * NT, row = row0 + q / CH, c = q % CH;
+      r[i] = bload8<T>(rs, row < lim ? (uint32_t)(((long long)row * ld + c * 8) * sizeof(T)) : OOB);
+    }
+  }
+  __device__ __forceinline__ void store(T* lds) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = t + i * NT, row = q / CH, c = q % CH;
+      store8(lds + row * HD + ((c ^ swz<HD>(row)) * 8), r[i]);
     }
   }
 };
@@ -166,48 +258,57 @@ __device__ __forceinline__ void store_acc_rows(T* __restrict__ dst_row, const f3
 }
 
 // ------------------------------------------------------------------ forward
-// Workgroup: 4 waves x QSUB 32-query sub-tiles (with QSUB = 2, wave w takes sub-tiles w and
-// 7 - w, pairing light and heavy rows of the causal triangle).  K/V tiles of 64 keys are double
-// buffered in LDS: each iteration writes tile j+1 (held in registers) and loads tile j+2 before
-// multiplying tile j.  Threads 0..127 move K (row layout), 128..255 move V (transposed).
-template <typename T, int HD, int QSUB>
-__global__ __launch_bounds__(ATHREADS, QSUB == 2 ? 1 : 2) void attn_fwd_kernel(
+// Workgroup: NWV waves x 32 queries.  K/V tiles of 64 keys are double buffered in LDS: each
+// iteration writes tile j+1 (held in registers) and loads tile j+2 before multiplying tile j.
+// bf16 (NWV = 8, two waves per SIMD): K and V as swizzled row tiles (V^T by transposing reads),
+// staged by the two halves of the workgroup.  fp32 (NWV = 4): threads 0..127 move K (padded
+// rows), 128..255 move V (transposed).
+template <typename T, int HD, int NWV>
+__global__ __launch_bounds__(64 * NWV, NWV == 8 ? 1 : 2) void attn_fwd_kernel(
     const T* __restrict__ qkv, T* __restrict__ out, float* __restrict__ lse2, int Tn, int H,
     float sl2) {
-  constexpr int BKV = 64, BQ = 128 * QSUB, PK = HD + pad<T>(), PV = BKV + pad<T>();
-  __shared__ __attribute__((aligned(16))) T Ks[2][BKV * PK];
-  __shared__ __attribute__((aligned(16))) T Vt[2][HD * PV];
+  constexpr int BKV = 64, BQ = 32 * NWV, PK = HD + pad<T>(), PV = BKV + pad<T>();
+  constexpr bool SW = sizeof(T) == 2;
+  static_assert(SW || NWV == 4, "the fp32 staging assumes 4 waves");
+  constexpr int KSZ = SW ? BKV * HD : BKV * PK, VSZ = SW ? BKV * HD : HD * PV;
+  __shared__ __attribute__((aligned(16))) T lds_all[2 * (KSZ + VSZ)];
+  auto Kbuf = [&](int b) { return lds_all + b * KSZ; };
+  auto Vbuf = [&](int b) { return lds_all + 2 * KSZ + b * VSZ; };
+  SwOffsets<HD> so;
+  if constexpr (SW) so.init(threadIdx.x % WAVE);
   const int D = H * HD;
   const long long ld = 3LL * D;
   const int qb = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE, lr = lane % 32, g = lane / 32;
   const T* base = qkv + (long long)b * Tn * ld;
 
-  int q0[QSUB];
-  vec8_t<T> qf[QSUB][HD / 16];
-  f32x16 o[QSUB][HD / 32];
-  float m[QSUB], l[QSUB];
+  const int q0 = qb * BQ + w * 32, q = q0 + lr;
+  vec8_t<T> qf[HD / 16];
+  f32x16 o[HD / 32];
+  float m = -INFINITY, l = 0.f;
+  {
+    const int qq = min(q, Tn - 1);
 #pragma unroll
-  for (int s = 0; s < QSUB; ++s) {
-    const int sub = QSUB == 2 ? (s == 0 ? w : 7 - w) : w;
-    q0[s] = qb * BQ + sub * 32;
-    const int q = min(q0[s] + lr, Tn - 1);
+    for (int c = 0; c < HD / 16; ++c) qf[c] = load8(base + (long long)qq * ld + h * HD + c * 16 + g * 8);
 #pragma unroll
-    for (int c = 0; c < HD / 16; ++c) qf[s][c] = load8(base + (long long)q * ld + h * HD + c * 16 + g * 8);
-#pragma unroll
-    for (int i = 0; i < HD / 32; ++i) o[s][i] = f32x16{};
-    m[s] = -INFINITY;
-    l[s] = 0.f;
+    for (int i = 0; i < HD / 32; ++i) o[i] = f32x16{};
   }
 
-  const bool is_v = threadIdx.x >= 128;
-  Tile88<T, BKV, HD> st;
-  st.init(is_v ? threadIdx.x - 128 : threadIdx.x, is_v);
+  constexpr int HALF = 32 * NWV;  // threads per tensor
+  const bool is_v = threadIdx.x >= HALF;
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(base + (is_v ? 2 * D : D) + h * HD, span_bytes<T>(Tn, ld, HD));
+  using Stage = typename std::conditional<SW, RowStage<T, BKV, HD, HALF>, Tile88<T, BKV, HD>>::type;
+  Stage st;
+  if constexpr (SW) st.init(is_v ? threadIdx.x - HALF : threadIdx.x);
+  else st.init(is_v ? threadIdx.x - HALF : threadIdx.x, is_v);
   auto put = [&](int buf) {
-    if (is_v) st.store_trans(Vt[buf], PV);
-    else st.store_rows(Ks[buf], PK);
+    if constexpr (SW) {
+      st.store(is_v ? Vbuf(buf) : Kbuf(buf));
+    } else {
+      if (is_v) st.store_trans(Vbuf(buf), PV);
+      else st.store_rows(Kbuf(buf), PK);
+    }
   };
   const int nkv = (min(Tn, (qb + 1) * BQ) - 1) / BKV + 1;
   st.load(rs, ld, 0, Tn);
@@ -220,20 +321,22 @@ __global__ __launch_bounds__(ATHREADS, QSUB == 2 ? 1 : 2) void attn_fwd_kernel(
     put(cur ^ 1);
     st.load(rs, ld, (j + 2) * BKV, Tn);
     __builtin_amdgcn_sched_barrier(0);
-    const T* K_ = Ks[cur];
-    const T* V_ = Vt[cur];
+    const T* K_ = Kbuf(cur);
+    const T* V_ = Vbuf(cur);
     // Scores are kept unscaled; the row max m is in the same unit, and the softmax weight is
     // 2^(sl2 * (s - m)) (sl2 = log2(e) / sqrt(Hd)).  Only the tile that crosses the diagonal
     // evaluates the causal mask.
-    auto tile = [&](auto diag_c, int s) {
+    auto tile = [&](auto diag_c) {
       constexpr bool DIAG = decltype(diag_c)::value;
-      const int q = q0[s] + lr;
       f32x16 sc[2];
 #pragma unroll
       for (int st2 = 0; st2 < 2; ++st2) {
         sc[st2] = f32x16{};
 #pragma unroll
-        for (int c = 0; c < HD / 16; ++c) mma<T>(sc[st2], frag_rows(K_, PK, st2 * 32 + lr, c * 16, g), qf[s][c]);
+        for (int c = 0; c < HD / 16; ++c) {
+          if constexpr (SW) mma<T>(sc[st2], frag_row_sw<HD>(K_, so, st2 * 32, c), qf[c]);
+          else mma<T>(sc[st2], frag_rows(K_, PK, st2 * 32 + lr, c * 16, g), qf[c]);
+        }
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -247,7 +350,7 @@ __global__ __launch_bounds__(ATHREADS, QSUB == 2 ? 1 : 2) void attn_fwd_kernel(
           mx = fmaxf(mx, sc[st2][r]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-      const float mn = fmaxf(m[s], mx);
+      const float mn = fmaxf(m, mx);
       const float nb = -mn * sl2;
       float sum = 0.f;
 #pragma unroll
@@ -260,45 +363,38 @@ __global__ __launch_bounds__(ATHREADS, QSUB == 2 ? 1 : 2) void attn_fwd_kernel(
         }
       sum += __shfl_xor(sum, 32, WAVE);
       // rescale the running output only when some row's max moved (rare after the first tiles)
-      if (!__all(mn == m[s])) {
-        const float alpha = fast_exp2((m[s] - mn) * sl2);
+      if (!__all(mn == m)) {
+        const float alpha = fast_exp2((m - mn) * sl2);
 #pragma unroll
         for (int dt = 0; dt < HD / 32; ++dt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[s][dt][r] *= alpha;
-        l[s] *= alpha;
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        l *= alpha;
       }
-      l[s] += sum;
-      m[s] = mn;
-      vec8_t<T> pf[2][2];
+      l += sum;
+      m = mn;
 #pragma unroll
       for (int st2 = 0; st2 < 2; ++st2)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) pf[st2][hh] = acc_frag<T>(sc[st2], hh);
+        for (int hh = 0; hh < 2; ++hh) {
+          const vec8_t<T> pf = acc_frag<T>(sc[st2], hh);
 #pragma unroll
-      for (int dt = 0; dt < HD / 32; ++dt)
-#pragma unroll
-        for (int st2 = 0; st2 < 2; ++st2)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-            mma<T>(o[s][dt], frag_split(V_, PV, dt * 32 + lr, st2 * 32 + hh * 16, g), pf[st2][hh]);
+          for (int dt = 0; dt < HD / 32; ++dt) {
+            if constexpr (SW) mma<T>(o[dt], frag_tr_sw<HD>(V_, so, st2 * 32 + hh * 16, dt), pf);
+            else mma<T>(o[dt], frag_split(V_, PV, dt * 32 + lr, st2 * 32 + hh * 16, g), pf);
+          }
+        }
     };
-#pragma unroll
-    for (int s = 0; s < QSUB; ++s) {
-      if (q0[s] >= Tn || kv0 > q0[s] + 31) continue;  // wave-uniform
-      if (kv0 + BKV - 1 > q0[s]) tile(std::true_type(), s);
-      else tile(std::false_type(), s);
+    if (q0 < Tn && kv0 <= q0 + 31) {  // wave-uniform
+      if (kv0 + BKV - 1 > q0) tile(std::true_type());
+      else tile(std::false_type());
     }
     __syncthreads();
   }
-#pragma unroll
-  for (int s = 0; s < QSUB; ++s) {
-    if (q0[s] >= Tn) continue;
-    const int q = q0[s] + lr;
-    T* dst = out + ((long long)b * Tn + q) * D + h * HD;
-    store_acc_rows<T, HD>(dst, o[s], 1.f / l[s], g);
-    if (g == 0) lse2[((long long)b * H + h) * Tn + q] = m[s] * sl2 + log2f(l[s]);
-  }
+  if (q0 >= Tn) return;
+  T* dst = out + ((long long)b * Tn + q) * D + h * HD;
+  store_acc_rows<T, HD>(dst, o, 1.f / l, g);
+  if (g == 0) lse2[((long long)b * H + h) * Tn + q] = m * sl2 + log2f(l);
 }
 
 // ------------------------------------------------------------------ backward
@@ -335,11 +431,18 @@ __global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dkdv_kernel(
     const float* __restrict__ dq_sum, T* __restrict__ dqkv, int Tn, int H, float sl2,
     float scale) {
   constexpr int BQ = 64, PR = HD + pad<T>(), PT = BQ + pad<T>();
-  __shared__ __attribute__((aligned(16))) T Qs[2][BQ * PR];
-  __shared__ __attribute__((aligned(16))) T Qt[2][HD * PT];
-  __shared__ __attribute__((aligned(16))) T Os[2][BQ * PR];
-  __shared__ __attribute__((aligned(16))) T Ot[2][HD * PT];
+  // bf16: Q and dO as swizzled row tiles, their transposes read by transposing reads; fp32: row
+  // (padded) and transposed copies of both.
+  constexpr bool SW = sizeof(T) == 2;
+  constexpr int RSZ = SW ? BQ * HD : BQ * PR, TSZ = SW ? 0 : HD * PT;
+  __shared__ __attribute__((aligned(16))) T lds_all[4 * RSZ + 4 * TSZ + 1];
+  auto Qs = [&](int b) { return lds_all + b * RSZ; };
+  auto Os = [&](int b) { return lds_all + (2 + b) * RSZ; };
+  auto Qt = [&](int b) { return lds_all + 4 * RSZ + b * TSZ; };
+  auto Ot = [&](int b) { return lds_all + 4 * RSZ + (2 + b) * TSZ; };
   __shared__ __attribute__((aligned(16))) float lse_s[2][BQ], dsum_s[2][BQ];
+  SwOffsets<HD> so;
+  if constexpr (SW) so.init(threadIdx.x % WAVE);
   const int D = H * HD;
   const long long ld = 3LL * D;
   const int kb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;  // key block 0 is the heaviest
@@ -383,8 +486,12 @@ __global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dkdv_kernel(
     }
   };
   auto put = [&](int buf) {
-    st.store_rows(is_o ? Os[buf] : Qs[buf], PR);
-    st.store_trans(is_o ? Ot[buf] : Qt[buf], PT);
+    if constexpr (SW) {
+      st.store_rows_sw(is_o ? Os(buf) : Qs(buf));
+    } else {
+      st.store_rows(is_o ? Os(buf) : Qs(buf), PR);
+      st.store_trans(is_o ? Ot(buf) : Qt(buf), PT);
+    }
     if (threadIdx.x < BQ) lse_s[buf][threadIdx.x] = stat;
     else if (threadIdx.x < 2 * BQ) dsum_s[buf][threadIdx.x - BQ] = stat;
   };
@@ -405,8 +512,13 @@ __global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dkdv_kernel(
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int c = 0; c < HD / 16; ++c) {
-        mma<T>(s, frag_rows(Qs[cur], PR, qs * 32 + lr, c * 16, g), kf[c]);
-        mma<T>(dp, frag_rows(Os[cur], PR, qs * 32 + lr, c * 16, g), vf[c]);
+        if constexpr (SW) {
+          mma<T>(s, frag_row_sw<HD>(Qs(cur), so, qs * 32, c), kf[c]);
+          mma<T>(dp, frag_row_sw<HD>(Os(cur), so, qs * 32, c), vf[c]);
+        } else {
+          mma<T>(s, frag_rows(Qs(cur), PR, qs * 32 + lr, c * 16, g), kf[c]);
+          mma<T>(dp, frag_rows(Os(cur), PR, qs * 32 + lr, c * 16, g), vf[c]);
+        }
       }
       // register r holds query qs*32 + (r/4)*8 + g*4 + r%4: statistics come as float4 groups
 #pragma unroll
@@ -433,8 +545,13 @@ __global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dkdv_kernel(
       for (int dt = 0; dt < HD / 32; ++dt)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          mma<T>(dv[dt], frag_split(Ot[cur], PT, dt * 32 + lr, qs * 32 + hh * 16, g), pf[hh]);
-          mma<T>(dk[dt], frag_split(Qt[cur], PT, dt * 32 + lr, qs * 32 + hh * 16, g), sf[hh]);
+          if constexpr (SW) {
+            mma<T>(dv[dt], frag_tr_sw<HD>(Os(cur), so, qs * 32 + hh * 16, dt), pf[hh]);
+            mma<T>(dk[dt], frag_tr_sw<HD>(Qs(cur), so, qs * 32 + hh * 16, dt), sf[hh]);
+          } else {
+            mma<T>(dv[dt], frag_split(Ot(cur), PT, dt * 32 + lr, qs * 32 + hh * 16, g), pf[hh]);
+            mma<T>(dk[dt], frag_split(Qt(cur), PT, dt * 32 + lr, qs * 32 + hh * 16, g), sf[hh]);
+          }
         }
     };
 #pragma unroll
@@ -460,9 +577,16 @@ __global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dq_kernel(
     const float* __restrict__ dq_sum, T* __restrict__ dqkv, int Tn, int H, float sl2,
     float scale) {
   constexpr int BKV = 64, PR = HD + pad<T>(), PT = BKV + pad<T>();
-  __shared__ __attribute__((aligned(16))) T Ks[2][BKV * PR];
-  __shared__ __attribute__((aligned(16))) T Vs[2][BKV * PR];
-  __shared__ __attribute__((aligned(16))) T Kt[2][HD * PT];
+  // bf16: K and V as swizzled row tiles, K^T read by transposing reads; fp32: padded rows plus a
+  // transposed copy of K.
+  constexpr bool SW = sizeof(T) == 2;
+  constexpr int RSZ = SW ? BKV * HD : BKV * PR, TSZ = SW ? 0 : HD * PT;
+  __shared__ __attribute__((aligned(16))) T lds_all[4 * RSZ + 2 * TSZ + 1];
+  auto Ks = [&](int b) { return lds_all + b * RSZ; };
+  auto Vs = [&](int b) { return lds_all + (2 + b) * RSZ; };
+  auto Kt = [&](int b) { return lds_all + 4 * RSZ + b * TSZ; };
+  SwOffsets<HD> so;
+  if constexpr (SW) so.init(threadIdx.x % WAVE);
   const int D = H * HD;
   const long long ld = 3LL * D;
   const int qb = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -492,11 +616,13 @@ __global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dq_kernel(
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(base + (is_v ? 2 * D : D) + h * HD, span_bytes<T>(Tn, ld, HD));
   auto put = [&](int buf) {
-    if (is_v) {
-      st.store_rows(Vs[buf], PR);
+    if constexpr (SW) {
+      st.store_rows_sw(is_v ? Vs(buf) : Ks(buf));
+    } else if (is_v) {
+      st.store_rows(Vs(buf), PR);
     } else {
-      st.store_rows(Ks[buf], PR);
-      st.store_trans(Kt[buf], PT);
+      st.store_rows(Ks(buf), PR);
+      st.store_trans(Kt(buf), PT);
     }
   };
   const int nkv = (min(Tn, (qb + 1) * 128) - 1) / BKV + 1;
@@ -518,8 +644,13 @@ __global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dq_kernel(
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int c = 0; c < HD / 16; ++c) {
-          mma<T>(s, frag_rows(Ks[cur], PR, st2 * 32 + lr, c * 16, g), qf[c]);
-          mma<T>(dp, frag_rows(Vs[cur], PR, st2 * 32 + lr, c * 16, g), of[c]);
+          if constexpr (SW) {
+            mma<T>(s, frag_row_sw<HD>(Ks(cur), so, st2 * 32, c), qf[c]);
+            mma<T>(dp, frag_row_sw<HD>(Vs(cur), so, st2 * 32, c), of[c]);
+          } else {
+            mma<T>(s, frag_rows(Ks(cur), PR, st2 * 32 + lr, c * 16, g), qf[c]);
+            mma<T>(dp, frag_rows(Vs(cur), PR, st2 * 32 + lr, c * 16, g), of[c]);
+          }
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -538,8 +669,10 @@ __global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dq_kernel(
 #pragma unroll
         for (int st2 = 0; st2 < 2; ++st2)
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-            mma<T>(dq[dt], frag_split(Kt[cur], PT, dt * 32 + lr, st2 * 32 + hh * 16, g), sf[st2][hh]);
+          for (int hh = 0; hh < 2; ++hh) {
+            if constexpr (SW) mma<T>(dq[dt], frag_tr_sw<HD>(Ks(cur), so, st2 * 32 + hh * 16, dt), sf[st2][hh]);
+            else mma<T>(dq[dt], frag_split(Kt(cur), PT, dt * 32 + lr, st2 * 32 + hh * 16, g), sf[st2][hh]);
+          }
     };
     if (active && kv0 <= q0 + 31) {
       if (kv0 + BKV - 1 > q0) tile(std::true_type());
@@ -573,11 +706,13 @@ template <typename T>
 gpt_status launch_attn_fwd(const T* qkv, T* out, float* lse2, int B, int Tn, int H, int hd,
                            hipStream_t s) {
   const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
-  // 32 queries per wave: two workgroups fit a CU, so one wave's softmax overlaps the other's
-  // MFMAs (measured faster at the d32 shape than 64 queries per wave at one workgroup per CU).
+  // 32 queries per wave, two waves per SIMD so that one wave's softmax overlaps the other's
+  // MFMAs: bf16 runs 8-wave workgroups (one per CU), fp32 4-wave workgroups (two per CU).
   gpt_status st = dispatch_hd<T>(hd, [&](auto HD) {
     constexpr int hdv = decltype(HD)::value;
-    attn_fwd_kernel<T, hdv, 1><<<dim3(cdiv(Tn, 128), H, B), ATHREADS, 0, s>>>(qkv, out, lse2, Tn, H, sl2);
+    constexpr int NWV = sizeof(T) == 2 ? 8 : 4;
+    attn_fwd_kernel<T, hdv, NWV><<<dim3(cdiv(Tn, 32 * NWV), H, B), 64 * NWV, 0, s>>>(
+        qkv, out, lse2, Tn, H, sl2);
   });
   return st != GPT_OK ? st : check_launch("attention fwd");
 }
