@@ -31,8 +31,19 @@ PEAK_HBM = 8.0e12        # MI355X HBM3E, B/s
 METRIC = "train tokens/sec (fwd+bwd) on 1 MI355X + MFU vs bf16 MFMA peak"
 DENSE = {"d32": configs.D32, "gpt2": configs.GPT2_SMALL, "tiny": configs.TINY}
 WORKLOADS = sorted(list(DENSE) + ["tables", "speedrun"])
-# Stages made of several kernels (their time is not one kernel's launch duration).
+# Stages made of several kernels (their time is not one kernel's launch duration); the weight-
+# gradient stages join them when their shape is split over K (see split_stages).
 MULTI_KERNEL = {"wte_segsum"}
+
+
+def split_stages(B, cfg):
+    """Weight-gradient stages whose GEMM runs split over K (partials + a reduce kernel)."""
+    if cfg.dtype != configs.BF16:
+        return set()
+    D, F, N, V = cfg.d_model, cfg.d_mlp, cfg.tokens, cfg.vocab
+    shapes = {"head_wgrad": (V, D, N), "down_wgrad": (D, F, N), "up_wgrad": (F, D, N),
+              "out_wgrad": (D, D, N), "qkv_wgrad": (3 * D, D, N), "tri_wgrad": (D, D, N)}
+    return {k for k, s in shapes.items() if B.gptk_gemm_wgrad_ws_floats(*s) > 0}
 
 
 def parse():
@@ -88,7 +99,7 @@ def _roof_entry(name, calls, tot_ms, flops, nbytes, bf16):
             "avg_launch_ms": round(per_launch_s * 1e3, 4), "algorithmic_per_launch": nbytes / calls}
 
 
-def profile_stages(B, ctx, step, n_steps, bf16):
+def profile_stages(B, ctx, step, n_steps, bf16, multi=frozenset()):
     """Instrumented pass: every launch bracketed by events on the step's stream.  Returns the
     dominant single-kernel stage's roofline and a per-stage table."""
     import torch
@@ -104,7 +115,7 @@ def profile_stages(B, ctx, step, n_steps, bf16):
         e = _roof_entry(n, c, m, f, b, bf16)
         parts[n] = {"ms_per_step": round(m / ps, 3), "launches": c // ps,
                     "achieved": e["achieved"], "unit": e["unit"], "frac": e["frac"]}
-    single = [s for s in stages if s[0] not in MULTI_KERNEL]
+    single = [s for s in stages if s[0] not in MULTI_KERNEL and s[0] not in multi]
     name, calls, tot_ms, flops, nbytes = max(single, key=lambda s: s[2])
     roof = _roof_entry(name, calls, tot_ms, flops, nbytes, bf16)
     roof["traffic"] = None
@@ -147,7 +158,7 @@ def bench_dense(a, B):
     ms, wall = time_steps(step, a.steps, a.warmup)
     lval = float(loss.item())
     assert np.isfinite(lval), lval
-    roof, parts = profile_stages(B, ctx, step, a.profile_steps, bf16)
+    roof, parts = profile_stages(B, ctx, step, a.profile_steps, bf16, split_stages(B, cfg))
 
     tok_s = cfg.tokens / (ms / 1e3)
     fpt = configs.flops_per_token(cfg)
@@ -346,7 +357,7 @@ def bench_speedrun(a, B):
     # stages of the dense micro-batch step
     roof, parts = profile_stages(B, ctx, lambda: B.gpt_fwd_bwd(
         ctx, t_in[0], t_tg[0], params, grads, loss, 1.0 / MB, 1, add_x0, add_v, add_tri,
-        d_x0[:N], d_v[:N]), a.profile_steps, True)
+        d_x0[:N], d_v[:N]), a.profile_steps, True, split_stages(B, cfg))
     n_tok = MB * N
     tok_s = n_tok / (ms / 1e3)
     fpt = configs.flops_per_token(cfg)

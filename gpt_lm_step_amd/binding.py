@@ -26,7 +26,7 @@ EXPORTS = [
 ]
 # Every symbol include/gpt_kernels.h declares.
 KERNEL_EXPORTS = [
-    "gptk_gemm", "gptk_rmsnorm_fwd", "gptk_rmsnorm_bwd", "gptk_rope_table",
+    "gptk_gemm", "gptk_gemm_wgrad", "gptk_gemm_wgrad_ws_floats", "gptk_rmsnorm_fwd", "gptk_rmsnorm_bwd", "gptk_rope_table",
     "gptk_rope_qknorm_fwd", "gptk_rope_qknorm_bwd", "gptk_attention_fwd", "gptk_attention_bwd",
     "gptk_softcap_ce",
 ]
@@ -80,6 +80,9 @@ def lib() -> C.CDLL:
             "gpt_last_error": (C.c_char_p, []),
             "gpt_status_string": (C.c_char_p, [i32]),
             "gptk_gemm": (i32, [i32, i32, i32, i32, i32, i32, vp, i64, vp, i64, vp, i64, i32, vp]),
+            "gptk_gemm_wgrad": (i32, [i32, i32, i32, i32, i32, i32, vp, i64, vp, i64, vp, i64, i32,
+                                      vp, i64, vp]),
+            "gptk_gemm_wgrad_ws_floats": (i64, [i32, i32, i32]),
             "gptk_rmsnorm_fwd": (i32, [i32, vp, vp, vp, i64, i32, f32, vp]),
             "gptk_rmsnorm_bwd": (i32, [i32, vp, vp, vp, vp, vp, vp, i64, i32, vp]),
             "gptk_rope_table": (i32, [i32, vp, vp, i32, i32, f32, vp]),
@@ -237,6 +240,17 @@ def gptk_gemm(a_kc: bool, b_kc: bool, M: int, N: int, K: int, A, lda: int, B, ld
               ldc: int, beta: int = 0, stream=None):
     _check(lib().gptk_gemm(_dtype_code(A), int(a_kc), int(b_kc), M, N, K, _ptr(A), lda, _ptr(B),
                            ldb, _ptr(C), ldc, int(beta), _stream(stream)))
+
+
+def gptk_gemm_wgrad_ws_floats(M: int, N: int, K: int) -> int:
+    return int(lib().gptk_gemm_wgrad_ws_floats(M, N, K))
+
+
+def gptk_gemm_wgrad(a_kc: bool, b_kc: bool, M: int, N: int, K: int, A, lda: int, B, ldb: int, C,
+                    ldc: int, beta: int = 0, ws=None, stream=None):
+    _check(lib().gptk_gemm_wgrad(_dtype_code(A), int(a_kc), int(b_kc), M, N, K, _ptr(A), lda,
+                                 _ptr(B), ldb, _ptr(C), ldc, int(beta), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def gptk_rmsnorm_fwd(x, y, rstd, eps: float = 1e-6, stream=None):

@@ -76,6 +76,18 @@ struct EpiStoreF32 {
   }
 };
 
+// Split-K partial: split blockIdx.y of the K range writes its fp32 [M][N] sum at
+// ws + blockIdx.y * stride (row pitch N).
+struct EpiSplit {
+  float* ws;
+  long long stride, ldo;
+  __device__ __forceinline__ void operator()(int r, int c, const float (&v)[4]) const {
+    float* p = ws + blockIdx.y * stride + (long long)r * ldo + c;
+    const float o[4] = {v[0], v[1], v[2], v[3]};
+    store4(p, o);
+  }
+};
+
 // out = res + acc (fp32 residual stream; out may equal res).
 struct EpiResid {
   const float* res;
@@ -490,9 +502,16 @@ struct DmaTile {
 // per CU.
 template <int BM, int BN, int WGM, int WGN, bool A_KC, bool B_KC, class Epi, int SITE>
 __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_dma_kernel(
-    const bf16* __restrict__ A, long long lda, const bf16* __restrict__ B, long long ldb, int M,
-    int N, int K, uint32_t a_bytes, uint32_t b_bytes, Epi epi) {
+    const bf16* A, long long lda, const bf16* B, long long ldb, int M,
+    int N, int K, uint32_t a_bytes, uint32_t b_bytes, Epi epi, int kps) {
   constexpr int NW = WGM * WGN, WTM = BM / WGM, WTN = BN / WGN;
+  // split-K: workgroups with blockIdx.y = s take K range [s * kps, min(K, (s + 1) * kps))
+  {
+    const int k0 = blockIdx.y * kps;
+    A += A_KC ? (long long)k0 : (long long)k0 * lda;
+    B += B_KC ? (long long)k0 : (long long)k0 * ldb;
+    K = min(K - k0, kps);
+  }
   constexpr int TM = WTM / 32, TN = WTN / 32, BK = 64;
   using TA = DmaTile<BM, A_KC, NW>;
   using TB = DmaTile<BN, B_KC, NW>;
@@ -610,13 +629,15 @@ inline long long operand_bytes(bool kc, long long rows, long long K, long long l
 
 template <int BM, int BN, int WGM, int WGN, class Epi, int SITE>
 void launch_dma(bool a_kc, bool b_kc, int M, int N, int K, const bf16* A, long long lda,
-                const bf16* B, long long ldb, const Epi& epi, hipStream_t s) {
-  dim3 grid((unsigned)(cdiv(M, BM) * cdiv(N, BN)));
-  const uint32_t ab = (uint32_t)operand_bytes(a_kc, M, K, lda, 2);
-  const uint32_t bb = (uint32_t)operand_bytes(b_kc, N, K, ldb, 2);
+                const bf16* B, long long ldb, const Epi& epi, hipStream_t s, int splits = 1) {
+  const int kps = splits > 1 ? (int)cdiv(cdiv(K, splits), 64) * 64 : K;  // K per split
+  dim3 grid((unsigned)(cdiv(M, BM) * cdiv(N, BN)), (unsigned)cdiv(K, kps));
+  // each split's operand spans at most these bytes from its own start
+  const uint32_t ab = (uint32_t)operand_bytes(a_kc, M, kps, lda, 2);
+  const uint32_t bb = (uint32_t)operand_bytes(b_kc, N, kps, ldb, 2);
 #define GEMM_DMA(AK, BK_)                                                                      \
   gemm_dma_kernel<BM, BN, WGM, WGN, AK, BK_, Epi, SITE><<<grid, 64 * WGM * WGN, 0, s>>>(        \
-      A, lda, B, ldb, M, N, K, ab, bb, epi)
+      A, lda, B, ldb, M, N, K, ab, bb, epi, kps)
   if (a_kc && b_kc) GEMM_DMA(true, true);
   else if (a_kc) GEMM_DMA(true, false);
   else if (b_kc) GEMM_DMA(false, true);
@@ -673,6 +694,91 @@ inline gpt_status gemm(bool a_kc, bool b_kc, int M, int N, int K, const T* A, lo
     gemm_detail::launch_tiles<T, 64, 64, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
   }
   return check_launch("gemm");
+}
+
+namespace gemm_detail {
+
+// Split-K for bf16 GEMMs with an fp32 output (weight gradients) whose output tiling alone leaves
+// CUs idle: prefer 256 x 256 tiles with 2..8 splits of >= 1024 K each when that gives >= 480
+// workgroups (about two per CU), else 128 x 128 tiles (two workgroups per CU) with up to 16
+// splits of >= 512 K.  A function of the shape only, so workspace sizing and launch agree.
+struct SplitPlan {
+  int splits;
+  bool big;
+};
+inline SplitPlan split_plan(int M, int N, int K) {
+  const long long t256 = (long long)cdiv(M, 256) * cdiv(N, 256);
+  if (t256 >= 240) return {1, true};
+  for (int sp = 2; sp <= 8; sp *= 2)
+    if (t256 * sp >= 480 && K / sp >= 1024) return {sp, true};
+  const long long t128 = (long long)cdiv(M, 128) * cdiv(N, 128);
+  int sp = 1;
+  while (sp < 16 && t128 * sp < 512 && K / (2 * sp) >= 512) sp *= 2;
+  return {sp, false};
+}
+
+// out[m][n] = (beta ? out[m][n] : 0) + sum over splits s (in order) of ws[s][m][n]; N % 4 == 0.
+template <int UNUSED = 0>
+__global__ void splitk_reduce_kernel(const float* __restrict__ ws, long long stride, int splits,
+                                     float* __restrict__ out, long long ldo, int M, int N,
+                                     int beta) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int n4 = N / 4;
+  if (i >= (long long)M * n4) return;
+  const long long r = i / n4;
+  const int c = (int)(i % n4) * 4;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(ws + r * N + c);
+  for (int sp = 1; sp < splits; ++sp) acc += *reinterpret_cast<const f32x4*>(ws + sp * stride + r * N + c);
+  f32x4* o = reinterpret_cast<f32x4*>(out + r * ldo + c);
+  if (beta) acc = *o + acc;
+  *o = acc;
+}
+
+}  // namespace gemm_detail
+
+// fp32 workspace (elements) a gemm_wgrad of this shape needs.
+inline long long gemm_wgrad_ws_floats(int M, int N, int K) {
+  const gemm_detail::SplitPlan sp = gemm_detail::split_plan(M, N, K);
+  return sp.splits > 1 ? (long long)sp.splits * M * N : 0;
+}
+
+// Weight-gradient GEMM (fp32 output, beta as in EpiStoreF32): bf16 shapes that leave CUs idle
+// are split over K into fp32 partials in `ws` and reduced in split order (deterministic).
+template <int SITE, typename T>
+inline gpt_status gemm_wgrad(bool a_kc, bool b_kc, int M, int N, int K, const T* A, long long lda,
+                             const T* B, long long ldb, const EpiStoreF32& epi, float* ws,
+                             long long ws_floats, hipStream_t s) {
+  if constexpr (!std::is_same<T, bf16>::value) {
+    return gemm<SITE, T>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
+  } else {
+    const gemm_detail::SplitPlan sp = gemm_detail::split_plan(M, N, K);
+    if (sp.splits == 1 || M <= 0 || N <= 0) return gemm<SITE, T>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
+    if (!ws || ws_floats < (long long)sp.splits * M * N)
+      return fail(GPT_EWORKSPACE, "gemm_wgrad: split-K workspace too small");
+    // same argument checks as gemm()
+    if (K <= 0 || K % 8) return fail(GPT_ESHAPE, "gemm: K must be a positive multiple of 8");
+    if (lda % 8 || ldb % 8) return fail(GPT_ESHAPE, "gemm: leading dimensions must be multiples of 8");
+    if ((!a_kc && M % 8) || (!b_kc && N % 8))
+      return fail(GPT_ESHAPE, "gemm: row-contiguous operands need a multiple of 8 rows");
+    if (N % 4 || epi.ldo % 4) return fail(GPT_ESHAPE, "gemm: N and ldo must be multiples of 4");
+    if (((uintptr_t)A | (uintptr_t)B) % 16 || ((uintptr_t)ws | (uintptr_t)epi.out) % 16)
+      return fail(GPT_EINVAL, "gemm: operands must be 16-byte aligned");
+    if (gemm_detail::operand_bytes(a_kc, M, K, lda, 2) > (1LL << 31) ||
+        gemm_detail::operand_bytes(b_kc, N, K, ldb, 2) > (1LL << 31))
+      return fail(GPT_ESHAPE, "gemm: each operand must span at most 2 GiB");
+    const long long stride = (long long)M * N;
+    const EpiSplit part{ws, stride, N};
+    if (sp.big)
+      gemm_detail::launch_dma<256, 256, 2, 4, EpiSplit, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, part, s, sp.splits);
+    else
+      gemm_detail::launch_dma<128, 128, 2, 2, EpiSplit, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, part, s, sp.splits);
+    const int kps = (int)cdiv(cdiv(K, sp.splits), 64) * 64;
+    const int used = (int)cdiv(K, kps);
+    const long long n = (long long)M * (N / 4);
+    gemm_detail::splitk_reduce_kernel<0><<<(unsigned)cdiv(n, 256), 256, 0, s>>>(ws, stride, used, epi.out,
+                                                                            epi.ldo, M, N, epi.beta);
+    return check_launch("gemm split-K");
+  }
 }
 
 }  // namespace gpt

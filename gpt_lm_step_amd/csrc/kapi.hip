@@ -23,6 +23,27 @@ gpt_status gptk_gemm(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32
   return gemm<G_TEST, float>(a_kc, b_kc, M, N, K, (const float*)A, lda, (const float*)B, ldb, epi, stream);
 }
 
+gpt_status gptk_gemm_wgrad(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32_t N,
+                           int32_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                           float* C, int64_t ldc, int32_t beta, float* ws, int64_t ws_floats,
+                           hipStream_t stream) {
+  if (bad_dtype(dtype) || !A || !B || !C) return fail(GPT_EINVAL, "gptk_gemm_wgrad: bad dtype or null");
+  if (M < 0 || N < 0 || K < 0 || ldc < N || ldc % 4) return fail(GPT_ESHAPE, "gptk_gemm_wgrad: bad sizes");
+  if (((uintptr_t)C) % 16) return fail(GPT_EINVAL, "gptk_gemm_wgrad: C must be 16-byte aligned");
+  if (ws_floats < 0) return fail(GPT_EINVAL, "gptk_gemm_wgrad: negative workspace size");
+  EpiStoreF32 epi{C, ldc, beta ? 1 : 0};
+  if (dtype == GPT_BF16)
+    return gemm_wgrad<G_TEST, bf16>(a_kc, b_kc, M, N, K, (const bf16*)A, lda, (const bf16*)B, ldb,
+                                    epi, ws, ws_floats, stream);
+  return gemm_wgrad<G_TEST, float>(a_kc, b_kc, M, N, K, (const float*)A, lda, (const float*)B,
+                                   ldb, epi, ws, ws_floats, stream);
+}
+
+int64_t gptk_gemm_wgrad_ws_floats(int32_t M, int32_t N, int32_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return gemm_wgrad_ws_floats(M, N, K);
+}
+
 gpt_status gptk_rmsnorm_fwd(int32_t dtype, const float* x, void* y, float* rstd, int64_t N,
                             int32_t D, float eps, hipStream_t stream) {
   if (bad_dtype(dtype) || !x || !y || !rstd) return fail(GPT_EINVAL, "gptk_rmsnorm_fwd: null");

@@ -100,6 +100,8 @@ struct Plan {
   int *n_valid, *err;
   void* seg_ws;
   size_t seg_bytes;
+  float* splitk;             // split-K partials of the weight-gradient GEMMs
+  long long splitk_floats;
   long long ce_rows;
 };
 
@@ -150,6 +152,15 @@ Plan carve_plan(const gpt_config& c, Carver& cv) {
   p.err = p.n_valid + 16;
   p.seg_bytes = segsum_workspace_bytes(N, (int)D);
   p.seg_ws = cv.take<char>(p.seg_bytes);
+  p.splitk_floats = 0;
+  if (c.dtype == GPT_BF16) {
+    const int n = (int)N, d = (int)D, f = (int)F;
+    const long long need[] = {gemm_wgrad_ws_floats(3 * d, d, n), gemm_wgrad_ws_floats(d, d, n),
+                              gemm_wgrad_ws_floats(d, f, n), gemm_wgrad_ws_floats(f, d, n),
+                              gemm_wgrad_ws_floats(c.vocab, d, (int)p.ce_rows)};
+    for (long long x : need) p.splitk_floats = std::max(p.splitk_floats, x);
+  }
+  p.splitk = p.splitk_floats ? cv.take<float>(p.splitk_floats) : nullptr;
   return p;
 }
 
@@ -291,8 +302,9 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
           gemm<G_HEAD_DGRAD, T>(true, false, rows, D, V, z, V, wh, D,
                                 EpiStoreF32{p.df + c0 * D, D, 0}, s));
     STAGE("head_wgrad", mm(V, D, rows), 0,
-          gemm<G_HEAD_WGRAD, T>(false, false, V, D, rows, z, V, f + c0 * D, D,
-                                EpiStoreF32{G + Ly.lm_head, D, (beta || c0 > 0) ? 1 : 0}, s));
+          gemm_wgrad<G_HEAD_WGRAD, T>(false, false, V, D, rows, z, V, f + c0 * D, D,
+                                      EpiStoreF32{G + Ly.lm_head, D, (beta || c0 > 0) ? 1 : 0},
+                                      p.splitk, p.splitk_floats, s));
   }
   STAGE("loss_reduce", 0, 4.0 * N, launch_loss_reduce(p.loss_rows, N, p.n_valid, loss, s));
   T* dx_t = (T*)p.dx_t;
@@ -310,14 +322,16 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
           gemm<G_DOWN_DGRAD, T>(true, false, (int)N, F, D, dx_t, D, P + Ly.wpr[l], F,
                                 EpiDRelu2<T>{hp, dact, F}, s));
     STAGE("down_wgrad", mm(D, F, N), 0,
-          gemm<G_DOWN_WGRAD, T>(false, false, D, F, (int)N, dx_t, D, act, F,
-                                EpiStoreF32{G + Ly.wpr[l], F, beta}, s));
+          gemm_wgrad<G_DOWN_WGRAD, T>(false, false, D, F, (int)N, dx_t, D, act, F,
+                                      EpiStoreF32{G + Ly.wpr[l], F, beta}, p.splitk,
+                                      p.splitk_floats, s));
     STAGE("up_dgrad", mm(N, D, F), 0,
           gemm<G_UP_DGRAD, T>(true, false, (int)N, D, F, dact, F, P + Ly.wfc[l], D,
                               EpiStoreF32{p.db, D, 0}, s));
     STAGE("up_wgrad", mm(F, D, N), 0,
-          gemm<G_UP_WGRAD, T>(false, false, F, D, (int)N, dact, F, bb, D,
-                              EpiStoreF32{G + Ly.wfc[l], D, beta}, s));
+          gemm_wgrad<G_UP_WGRAD, T>(false, false, F, D, (int)N, dact, F, bb, D,
+                                    EpiStoreF32{G + Ly.wfc[l], D, beta}, p.splitk,
+                                    p.splitk_floats, s));
     STAGE("rmsnorm_bwd", 0, ND * (16 + es) + 4.0 * N,
           launch_rms_bwd<T>(b.x_mid, b.rstd_b, p.db, p.dx, p.dx, dx_t, N, D, s));
     // attention: x_mid = x_in + O Wo^T
@@ -325,8 +339,9 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
           gemm<G_OUT_DGRAD, T>(true, false, (int)N, D, D, dx_t, D, P + Ly.wo[l], D,
                                EpiStore<T>{dO, D}, s));
     STAGE("out_wgrad", mm(D, D, N), 0,
-          gemm<G_OUT_WGRAD, T>(false, false, D, D, (int)N, dx_t, D, o, D,
-                               EpiStoreF32{G + Ly.wo[l], D, beta}, s));
+          gemm_wgrad<G_OUT_WGRAD, T>(false, false, D, D, (int)N, dx_t, D, o, D,
+                                     EpiStoreF32{G + Ly.wo[l], D, beta}, p.splitk,
+                                     p.splitk_floats, s));
     STAGE("attn_bwd_pre", 0, 2.0 * ND * es + 4.0 * N * H,
           launch_attn_bwd_stage<T>(0, qkv, o, dO, b.lse, p.dqsum, dqkv, Bn, Tn, H, hd, s));
     STAGE("attn_bwd_dkdv", 8.0 * pairs * hd, 0,
@@ -342,8 +357,9 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
           gemm<G_QKV_DGRAD, T>(true, false, (int)N, D, 3 * D, dqkv, 3 * D, P + Ly.wqkv[l], D,
                                EpiStoreF32{p.db, D, 0}, s));
     STAGE("qkv_wgrad", mm(3 * D, D, N), 0,
-          gemm<G_QKV_WGRAD, T>(false, false, 3 * D, D, (int)N, dqkv, 3 * D, a, D,
-                               EpiStoreF32{G + Ly.wqkv[l], D, beta}, s));
+          gemm_wgrad<G_QKV_WGRAD, T>(false, false, 3 * D, D, (int)N, dqkv, 3 * D, a, D,
+                                     EpiStoreF32{G + Ly.wqkv[l], D, beta}, p.splitk,
+                                     p.splitk_floats, s));
     STAGE("rmsnorm_bwd", 0, ND * (16 + es) + 4.0 * N,
           launch_rms_bwd<T>(b.x_in, b.rstd_a, p.db, p.dx, p.dx, dx_t, N, D, s));
   }
@@ -364,8 +380,9 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
       T* du_t = (T*)p.du_t;
       STAGE("cast", 0, ND * (4 + es), launch_cast<T>(du_t, p.dU, N * D, s));
       STAGE("tri_wgrad", mm(D, D, N), 0,
-            gemm<G_TRI_WGRAD, T>(false, false, D, D, (int)N, du_t, D, tri_rows, D,
-                                 EpiStoreF32{G + Ly.wtri, D, beta}, s));
+            gemm_wgrad<G_TRI_WGRAD, T>(false, false, D, D, (int)N, du_t, D, tri_rows, D,
+                                       EpiStoreF32{G + Ly.wtri, D, beta}, p.splitk,
+                                       p.splitk_floats, s));
     }
   }
 #undef STAGE

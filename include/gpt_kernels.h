@@ -22,6 +22,19 @@ gpt_status gptk_gemm(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32
                      const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
                      int64_t ldc, int32_t beta, hipStream_t stream);
 
+/* The weight-gradient form of gptk_gemm (same operands, result and argument rules; N and ldc
+ * multiples of 4): bf16 shapes whose output tiling alone would leave compute units idle are
+ * split over K, each split writing an fp32 partial [M,N] into `ws`, and the partials are added
+ * in split order (deterministic), then written to C or added to it (beta).  ws: caller-owned
+ * device fp32 buffer of at least gptk_gemm_wgrad_ws_floats(M, N, K) elements (NULL allowed when
+ * that is 0); GPT_EWORKSPACE if it is smaller.  fp32 operands never split. */
+gpt_status gptk_gemm_wgrad(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32_t N,
+                           int32_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                           float* C, int64_t ldc, int32_t beta, float* ws, int64_t ws_floats,
+                           hipStream_t stream);
+/* fp32 elements of split-K workspace gptk_gemm_wgrad needs for a bf16 M x N x K product. */
+int64_t gptk_gemm_wgrad_ws_floats(int32_t M, int32_t N, int32_t K);
+
 /* RMSNorm without weight (`norm` of the nanochat GPT class): x fp32 [N,D] -> y T [N,D],
  * rstd fp32 [N] = 1/sqrt(mean(x^2) + eps).  D a multiple of 64, at most 2048. */
 gpt_status gptk_rmsnorm_fwd(int32_t dtype, const float* x, void* y, float* rstd, int64_t N,

@@ -111,3 +111,12 @@ def test_table_entry_point_validation():
 def test_status_strings():
     for s in (B.GPT_OK, B.GPT_EINVAL, B.GPT_ESHAPE, B.GPT_ERANGE, B.GPT_EWORKSPACE, B.GPT_EHIP):
         assert B.lib().gpt_status_string(s).decode() not in ("", "unknown status")
+
+
+@pytest.mark.parametrize("M,N,K,splits", [
+    (768, 768, 8192, 16), (2304, 768, 8192, 8), (2048, 2048, 16384, 8), (6144, 2048, 65536, 4),
+    (2048, 8192, 65536, 1), (50304, 768, 8192, 1), (256, 384, 128, 1), (768, 768, 1024, 2), (768, 768, 1016, 1)])
+def test_wgrad_split_k_workspace(M, N, K, splits):
+    """Split-K weight-gradient plan: one fp32 M x N partial per split, none when not split."""
+    assert B.gptk_gemm_wgrad_ws_floats(M, N, K) == (splits * M * N if splits > 1 else 0)
+    assert B.gptk_gemm_wgrad_ws_floats(0, N, K) == 0

@@ -64,6 +64,35 @@ def test_gemm_large_square_bf16():
     assert rel_l2(host(c), want) < 2e-6
 
 
+@pytest.mark.parametrize("a_kc,b_kc,M,N,K,splits", [
+    (0, 0, 768, 768, 8192, 16),     # 128-tile plan, 16 splits (GPT-2-small output projection)
+    (0, 0, 2304, 768, 8192, 8),     # 128-tile plan, 8 splits
+    (0, 0, 2048, 2048, 16384, 8),   # 256-tile plan, 8 splits
+    (1, 0, 392, 520, 4104, 8),      # ragged M, N and a last split shorter than the others
+    (0, 1, 264, 136, 2056, 4),
+    (1, 1, 256, 384, 128, 1),       # too short to split
+])
+def test_gemm_wgrad_split_k(a_kc, b_kc, M, N, K, splits):
+    """Split-K weight-gradient GEMM against fp64, overwrite then accumulate; the plan's split
+    count is the one the step uses for such shapes."""
+    need = B.gptk_gemm_wgrad_ws_floats(M, N, K)
+    assert need == (splits * M * N if splits > 1 else 0)
+    a, ta = _operand(41, M, K, a_kc, BF)
+    b, tb = _operand(42, N, K, b_kc, BF)
+    lda, ldb = (K if a_kc else M), (K if b_kc else N)
+    ws = torch.full((max(need, 4),), float("nan"), device="cuda")
+    c = torch.full((M, N), float("nan"), device="cuda")
+    B.gptk_gemm_wgrad(a_kc, b_kc, M, N, K, ta, lda, tb, ldb, c, N, beta=0, ws=ws)
+    want = a.astype(np.float64) @ b.astype(np.float64).T
+    assert rel_l2(host(c), want) < 1e-5
+    B.gptk_gemm_wgrad(a_kc, b_kc, M, N, K, ta, lda, tb, ldb, c, N, beta=1, ws=ws)
+    assert rel_l2(host(c), 2 * want) < 1e-5
+    if need:
+        small = torch.empty(need - 4, device="cuda")
+        with pytest.raises(B.GptError):
+            B.gptk_gemm_wgrad(a_kc, b_kc, M, N, K, ta, lda, tb, ldb, c, N, ws=small)
+
+
 @pytest.mark.parametrize("dtype", [BF, F32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("D", [64, 128, 768, 2048])
 def test_rmsnorm_fwd_bwd(dtype, D):
