@@ -132,6 +132,10 @@ __device__ __forceinline__ bf16x8 frag_tr_sw(const bf16* lds, const SwOffsets<HD
   return v;
 }
 
+// Index of the calling wave, known to the compiler to be the same in every lane (so values derived
+// from it, such as buffer resources, live in scalar registers instead of per-lane loops).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x / WAVE); }
+
 // 2^x with the hardware instruction (v_exp_f32; results below 2^-126 flush to 0, 2^-inf = 0).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -295,7 +299,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 8 ? 1 : 2) void attn_fwd_kernel(
   }
 
   constexpr int HALF = 32 * NWV;  // threads per tensor
-  const bool is_v = threadIdx.x >= HALF;
+  const bool is_v = wave_id() >= NWV / 2;  // wave-uniform: buffer resources stay scalar
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(base + (is_v ? 2 * D : D) + h * HD, span_bytes<T>(Tn, ld, HD));
   using Stage = typename std::conditional<SW, RowStage<T, BKV, HD, HALF>, Tile88<T, BKV, HD>>::type;
@@ -470,7 +474,7 @@ __global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dkdv_kernel(
     dv[i] = f32x16{};
   }
 
-  const bool is_o = threadIdx.x >= 128;
+  const bool is_o = wave_id() >= 2;  // wave-uniform: buffer resources stay scalar
   const int tl = is_o ? threadIdx.x - 128 : threadIdx.x;
   Tile88<T, BQ, HD> st;
   st.init(tl, false);
@@ -610,7 +614,7 @@ __global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dq_kernel(
 #pragma unroll
   for (int i = 0; i < HD / 32; ++i) dq[i] = f32x16{};
 
-  const bool is_v = threadIdx.x >= 128;
+  const bool is_v = wave_id() >= 2;  // wave-uniform: buffer resources stay scalar
   Tile88<T, BKV, HD> st;
   st.init(is_v ? threadIdx.x - 128 : threadIdx.x, false);
   const __amdgpu_buffer_rsrc_t rs =
