@@ -282,7 +282,8 @@ __global__ __launch_bounds__(64 * NWV, NWV == 8 ? 1 : 2) void attn_fwd_kernel(
   if constexpr (SW) so.init(threadIdx.x % WAVE);
   const int D = H * HD;
   const long long ld = 3LL * D;
-  const int qb = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // grid (H*B, query blocks): the heaviest query block of every head is dispatched first
+  const int qb = gridDim.y - 1 - blockIdx.y, h = blockIdx.x % H, b = blockIdx.x / H;
   const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE, lr = lane % 32, g = lane / 32;
   const T* base = qkv + (long long)b * Tn * ld;
 
@@ -449,7 +450,8 @@ __global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dkdv_kernel(
   if constexpr (SW) so.init(threadIdx.x % WAVE);
   const int D = H * HD;
   const long long ld = 3LL * D;
-  const int kb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;  // key block 0 is the heaviest
+  // grid (H*B, key blocks): key block 0, the heaviest, of every head is dispatched first
+  const int kb = blockIdx.y, h = blockIdx.x % H, b = blockIdx.x / H;
   const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE, lr = lane % 32, g = lane / 32;
   const int k0 = kb * 128 + w * 32, key = k0 + lr;
   const bool active = k0 < Tn;
@@ -573,6 +575,208 @@ __global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dkdv_kernel(
   store_acc_rows<T, HD>(row + 2 * D, dv, 1.f, g);
 }
 
+// Instruction order for one steady-state iteration of the pipelined backward kernels: the
+// statistics and the first operand fragments are read, then each matrix-core instruction of the
+// S/dP products is followed by a share of the softmax-backward vector work and one fragment read
+// (so vector ALU and matrix cores overlap and few fragments are live at once), then the dV/dK (or
+// dQ) products consume their transposed fragments two reads ahead.
+template <int HD>
+__device__ __forceinline__ void pipe_schedule() {
+  constexpr int NA = 2 * (HD / 16);  // S/dP matrix-core instructions
+  constexpr int NC = 4 * (HD / 32);  // dV/dK matrix-core instructions
+  __builtin_amdgcn_sched_group_barrier(0x100, 8 + 4, 0);  // DS read: statistics, first fragments
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  }
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read (transposing)
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+  }
+}
+
+// bf16 dK, dV, software pipelined.  4 waves x 32 keys (keys on lanes, as above) walk 32-query
+// tiles held in a ring of four LDS slots (Q and dO as swizzled row tiles, plus the tile's LSE and
+// rowsum(dO*O)).  In iteration j a wave turns S_j, dP_j into P_j, dS_j (vector ALU) while the
+// matrix cores compute S_{j+1}, dP_{j+1} from slot j+1, then accumulates dV += P_j^T dO_j and
+// dK += dS_j^T Q_j.  Every wave runs every tile: on tiles before its diagonal the causal mask
+// zeroes P and dS, so they add nothing, and the loop body has no branches (the two S/dP register
+// sets stay fixed).  The loop is unrolled by four so each slot's LDS offset is a constant folded
+// into the read instructions.  One barrier per tile: slot j+3 is written while j and j+1 are read.
+// Sequence length: a multiple of 64.
+template <int HD>
+__global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dkdv_pipe_kernel(
+    const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const float* __restrict__ lse2,
+    const float* __restrict__ dq_sum, bf16* __restrict__ dqkv, int Tn, int H, float sl2,
+    float scale) {
+  constexpr int BQ = 32, NSLOT = 4, TS = BQ * HD;  // TS: elements of one tensor tile
+  constexpr int STAT_BYTES = NSLOT * 2 * BQ * 4;
+  // statistics first so that every tile offset fits a read instruction's immediate offset
+  __shared__ __attribute__((aligned(16))) char lds_raw[STAT_BYTES + NSLOT * 2 * TS * 2];
+  float* stat_s = reinterpret_cast<float*>(lds_raw);  // [slot][LSE, rowsum][BQ]
+  bf16* lds_all = reinterpret_cast<bf16*>(lds_raw + STAT_BYTES);
+  SwOffsets<HD> so;
+  so.init(threadIdx.x % WAVE);
+  const int D = H * HD;
+  const long long ld = 3LL * D;
+  // grid (H*B, key blocks): key block 0, the heaviest, of every head is dispatched first
+  const int kb = blockIdx.y, h = blockIdx.x % H, b = blockIdx.x / H;
+  const int lane = threadIdx.x % WAVE, w = wave_id(), lr = lane % 32, g = lane / 32;
+  const int qstart = kb * 128, k0 = qstart + w * 32, key = k0 + lr;
+  const bf16* base = qkv + (long long)b * Tn * ld;
+  const bf16* dbase = dout + (long long)b * Tn * D;
+  const float* lrow = lse2 + ((long long)b * H + h) * Tn;
+  const float* drow = dq_sum + ((long long)b * H + h) * Tn;
+
+  bf16x8 kf[HD / 16], vf[HD / 16];
+  {
+    const int kk = min(key, Tn - 1);
+#pragma unroll
+    for (int c = 0; c < HD / 16; ++c) {
+      kf[c] = load8(base + (long long)kk * ld + D + h * HD + c * 16 + g * 8);
+      vf[c] = load8(base + (long long)kk * ld + 2 * D + h * HD + c * 16 + g * 8);
+    }
+  }
+  f32x16 dk[HD / 32], dv[HD / 32];
+#pragma unroll
+  for (int i = 0; i < HD / 32; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
+
+  // waves 0-1 stage Q (threads 0..63 also the LSE and rowsum(dO*O) of the tile), waves 2-3 dO
+  const bool is_o = w >= 2;
+  RowStage<bf16, BQ, HD, 128> st;
+  st.init(threadIdx.x % 128);
+  const __amdgpu_buffer_rsrc_t rs = is_o ? make_rsrc(dbase + h * HD, span_bytes<bf16>(Tn, D, HD))
+                                         : make_rsrc(base + h * HD, span_bytes<bf16>(Tn, ld, HD));
+  const long long sld = is_o ? (long long)D : ld;
+  float stat = 0.f;
+  auto fetch = [&](int t) {
+    const int q0 = qstart + t * BQ;
+    st.load(rs, sld, q0, Tn);
+    if (threadIdx.x < 2 * BQ) {
+      const int qi = q0 + threadIdx.x % BQ;
+      stat = qi < Tn ? (threadIdx.x < BQ ? lrow[qi] : drow[qi]) : 0.f;
+    }
+  };
+  auto put = [&](int slot) {
+    st.store(lds_all + slot * 2 * TS + (is_o ? TS : 0));
+    if (threadIdx.x < 2 * BQ) stat_s[slot * 2 * BQ + threadIdx.x] = stat;
+  };
+
+  // S = Q K^T and dP = dO V^T of the tile in slot SL (32 queries x 32 keys)
+  auto stage_a = [&](auto sl_c, f32x16& sa, f32x16& da) {
+    const bf16* Q_ = lds_all + decltype(sl_c)::value * 2 * TS;
+    const bf16* O_ = Q_ + TS;
+    sa = f32x16{};
+    da = f32x16{};
+#pragma unroll
+    for (int c = 0; c < HD / 16; ++c) {
+      mma<bf16>(sa, frag_row_sw<HD>(Q_, so, 0, c), kf[c]);
+      mma<bf16>(da, frag_row_sw<HD>(O_, so, 0, c), vf[c]);
+    }
+  };
+  // P = 2^(S sl2 - LSE2) (causally masked), dS = P (dP - rowsum(dO*O)), as bf16 operands with
+  // the accumulator's K permutation (register r holds query (r/4)*8 + g*4 + r%4 of the tile)
+  auto stage_b = [&](auto sl_c, int t, f32x16& sa, f32x16& da, bf16x8 (&pf)[2],
+                     bf16x8 (&sf)[2]) {
+    const float* st_ = stat_s + decltype(sl_c)::value * 2 * BQ;
+    const int kq = key - (qstart + t * BQ);  // key - first query of the tile
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int qb4 = r4 * 8 + g * 4;
+      const f32x4 ls = *reinterpret_cast<const f32x4*>(st_ + qb4);
+      const f32x4 dsm = *reinterpret_cast<const f32x4*>(st_ + BQ + qb4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r4 * 4 + i;
+        float p = fast_exp2(fmaf(sa[r], sl2, -ls[i]));
+        if (kq > qb4 + i) p = 0.f;
+        sa[r] = p;
+        da[r] = p * (da[r] - dsm[i]);
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      pf[hh] = acc_frag<bf16>(sa, hh);
+      sf[hh] = acc_frag<bf16>(da, hh);
+    }
+  };
+  // dV^T += dO^T P, dK^T += Q^T dS for the tile in slot SL
+  auto stage_c = [&](auto sl_c, const bf16x8 (&pf)[2], const bf16x8 (&sf)[2]) {
+    const bf16* Q_ = lds_all + decltype(sl_c)::value * 2 * TS;
+    const bf16* O_ = Q_ + TS;
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        mma<bf16>(dv[dt], frag_tr_sw<HD>(O_, so, hh * 16, dt), pf[hh]);
+        mma<bf16>(dk[dt], frag_tr_sw<HD>(Q_, so, hh * 16, dt), sf[hh]);
+      }
+  };
+
+  const int nq = (Tn - qstart) / BQ;  // even
+  // prologue: tiles 0..2 in slots 0..2, tile 3 in registers
+  fetch(0);
+  put(0);
+#pragma unroll
+  for (int t = 1; t < 3; ++t)
+    if (t < nq) {
+      fetch(t);
+      put(t);
+    }
+  if (3 < nq) fetch(3);
+  __syncthreads();
+
+  // iteration j (slot SL = j % 4): B and C on tile j, A on tile j + 1 when HAS_A
+  auto iter = [&](auto sl_c, auto has_a_c, int j, f32x16& sc, f32x16& dc, f32x16& sn,
+                  f32x16& dn) {
+    constexpr int SL = decltype(sl_c)::value;
+    constexpr bool HAS_A = decltype(has_a_c)::value;
+    if (j + 3 < nq) put((SL + 3) % NSLOT);
+    if (j + 4 < nq) fetch(j + 4);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 pf[2], sf[2];
+    stage_b(sl_c, j, sc, dc, pf, sf);
+    if constexpr (HAS_A) stage_a(std::integral_constant<int, (SL + 1) % NSLOT>(), sn, dn);
+    stage_c(sl_c, pf, sf);
+    if constexpr (HAS_A) pipe_schedule<HD>();
+    __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using YES = std::true_type;
+  using NO = std::false_type;
+  f32x16 s0, d0, s1, d1;
+  stage_a(I0(), s0, d0);
+  int j = 0;
+  for (; j + 4 < nq; j += 4) {
+    iter(I0(), YES(), j, s0, d0, s1, d1);
+    iter(I1(), YES(), j + 1, s1, d1, s0, d0);
+    iter(I2(), YES(), j + 2, s0, d0, s1, d1);
+    iter(I3(), YES(), j + 3, s1, d1, s0, d0);
+  }
+  if (nq - j == 4) {
+    iter(I0(), YES(), j, s0, d0, s1, d1);
+    iter(I1(), YES(), j + 1, s1, d1, s0, d0);
+    iter(I2(), YES(), j + 2, s0, d0, s1, d1);
+    iter(I3(), NO(), j + 3, s1, d1, s0, d0);
+  } else {
+    iter(I0(), YES(), j, s0, d0, s1, d1);
+    iter(I1(), NO(), j + 1, s1, d1, s0, d0);
+  }
+  if (k0 >= Tn) return;
+  bf16* row = dqkv + ((long long)b * Tn + key) * ld + h * HD;
+  store_acc_rows<bf16, HD>(row + D, dk, scale, g);
+  store_acc_rows<bf16, HD>(row + 2 * D, dv, 1.f, g);
+}
+
 // dQ for 128 queries per workgroup (4 waves x 32), looping over 64-key tiles double buffered in
 // LDS (K in row and transposed layout, V in row layout).  Threads 0..127 move K, 128..255 V.
 template <typename T, int HD>
@@ -593,7 +797,8 @@ __global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dq_kernel(
   if constexpr (SW) so.init(threadIdx.x % WAVE);
   const int D = H * HD;
   const long long ld = 3LL * D;
-  const int qb = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // grid (H*B, query blocks): the heaviest query block of every head is dispatched first
+  const int qb = gridDim.y - 1 - blockIdx.y, h = blockIdx.x % H, b = blockIdx.x / H;
   const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE, lr = lane % 32, g = lane / 32;
   const int q0 = qb * 128 + w * 32, q = q0 + lr;
   const bool active = q0 < Tn;
@@ -715,7 +920,7 @@ gpt_status launch_attn_fwd(const T* qkv, T* out, float* lse2, int B, int Tn, int
   gpt_status st = dispatch_hd<T>(hd, [&](auto HD) {
     constexpr int hdv = decltype(HD)::value;
     constexpr int NWV = sizeof(T) == 2 ? 8 : 4;
-    attn_fwd_kernel<T, hdv, NWV><<<dim3(cdiv(Tn, 32 * NWV), H, B), 64 * NWV, 0, s>>>(
+    attn_fwd_kernel<T, hdv, NWV><<<dim3(H * B, cdiv(Tn, 32 * NWV)), 64 * NWV, 0, s>>>(
         qkv, out, lse2, Tn, H, sl2);
   });
   return st != GPT_OK ? st : check_launch("attention fwd");
@@ -728,14 +933,19 @@ gpt_status launch_attn_bwd_stage(int stage, const T* qkv, const T* out, const T*
   const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
   const float scale = 1.f / sqrtf((float)hd);
   const long long N = (long long)B * Tn;
-  dim3 grid(cdiv(Tn, 128), H, B);
+  dim3 grid(H * B, cdiv(Tn, 128));
   gpt_status st = dispatch_hd<T>(hd, [&](auto HD) {
     constexpr int hdv = decltype(HD)::value;
     if (stage == 0)
       attn_bwd_pre_kernel<T, hdv><<<cdiv(N * H, 256), 256, 0, s>>>(out, dout, dq_sum, N, Tn, H);
-    else if (stage == 1)
-      attn_bwd_dkdv_kernel<T, hdv><<<grid, ATHREADS, 0, s>>>(qkv, dout, lse2, dq_sum, dqkv, Tn, H,
-                                                             sl2, scale);
+    else if (stage == 1) {
+      if constexpr (std::is_same<T, bf16>::value)
+        attn_bwd_dkdv_pipe_kernel<hdv><<<grid, ATHREADS, 0, s>>>(qkv, dout, lse2, dq_sum, dqkv, Tn,
+                                                                 H, sl2, scale);
+      else
+        attn_bwd_dkdv_kernel<T, hdv><<<grid, ATHREADS, 0, s>>>(qkv, dout, lse2, dq_sum, dqkv, Tn,
+                                                               H, sl2, scale);
+    }
     else
       attn_bwd_dq_kernel<T, hdv><<<grid, ATHREADS, 0, s>>>(qkv, dout, lse2, dq_sum, dqkv, Tn, H,
                                                            sl2, scale);
