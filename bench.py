@@ -46,6 +46,13 @@ def split_stages(B, cfg):
     return {k for k, s in shapes.items() if B.gptk_gemm_wgrad_ws_floats(*s) > 0}
 
 
+def multi_stages(B, cfg):
+    """Stages that launch more than one kernel for this configuration."""
+    # the fp32 attention backward computes rowsum(dO*O) in a kernel of its own before dQ
+    extra = set() if cfg.dtype == configs.BF16 else {"attn_bwd_dq"}
+    return split_stages(B, cfg) | extra
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,7 +165,7 @@ def bench_dense(a, B):
     ms, wall = time_steps(step, a.steps, a.warmup)
     lval = float(loss.item())
     assert np.isfinite(lval), lval
-    roof, parts = profile_stages(B, ctx, step, a.profile_steps, bf16, split_stages(B, cfg))
+    roof, parts = profile_stages(B, ctx, step, a.profile_steps, bf16, multi_stages(B, cfg))
 
     tok_s = cfg.tokens / (ms / 1e3)
     fpt = configs.flops_per_token(cfg)
@@ -357,7 +364,7 @@ def bench_speedrun(a, B):
     # stages of the dense micro-batch step
     roof, parts = profile_stages(B, ctx, lambda: B.gpt_fwd_bwd(
         ctx, t_in[0], t_tg[0], params, grads, loss, 1.0 / MB, 1, add_x0, add_v, add_tri,
-        d_x0[:N], d_v[:N]), a.profile_steps, True, split_stages(B, cfg))
+        d_x0[:N], d_v[:N]), a.profile_steps, True, multi_stages(B, cfg))
     n_tok = MB * N
     tok_s = n_tok / (ms / 1e3)
     fpt = configs.flops_per_token(cfg)

@@ -580,11 +580,10 @@ __global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dkdv_kernel(
 // S/dP products is followed by a share of the softmax-backward vector work and one fragment read
 // (so vector ALU and matrix cores overlap and few fragments are live at once), then the dV/dK (or
 // dQ) products consume their transposed fragments two reads ahead.
-template <int HD>
+template <int NA, int NC, int NFIRST>
 __device__ __forceinline__ void pipe_schedule() {
-  constexpr int NA = 2 * (HD / 16);  // S/dP matrix-core instructions
-  constexpr int NC = 4 * (HD / 32);  // dV/dK matrix-core instructions
-  __builtin_amdgcn_sched_group_barrier(0x100, 8 + 4, 0);  // DS read: statistics, first fragments
+  // NA: S/dP matrix-core instructions; NC: dV/dK (or dQ) ones; NFIRST: reads issued up front
+  __builtin_amdgcn_sched_group_barrier(0x100, NFIRST, 0);  // DS read: statistics, first fragments
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -744,7 +743,7 @@ __global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dkdv_pipe_kernel(
     stage_b(sl_c, j, sc, dc, pf, sf);
     if constexpr (HAS_A) stage_a(std::integral_constant<int, (SL + 1) % NSLOT>(), sn, dn);
     stage_c(sl_c, pf, sf);
-    if constexpr (HAS_A) pipe_schedule<HD>();
+    if constexpr (HAS_A) pipe_schedule<2 * (HD / 16), 4 * (HD / 32), 8 + 4>();
     __syncthreads();
   };
   using I0 = std::integral_constant<int, 0>;
@@ -775,6 +774,151 @@ __global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dkdv_pipe_kernel(
   bf16* row = dqkv + ((long long)b * Tn + key) * ld + h * HD;
   store_acc_rows<bf16, HD>(row + D, dk, scale, g);
   store_acc_rows<bf16, HD>(row + 2 * D, dv, 1.f, g);
+}
+
+// bf16 dQ, software pipelined, with rowsum(dO*O) fused in.  4 waves x 32 queries (queries on
+// lanes, as in the forward) walk 32-key tiles held in a ring of four LDS slots (K and V as swizzled
+// row tiles).  In iteration j a wave turns S_j^T, dP_j^T into dS_j^T (vector ALU) while the matrix
+// cores compute S_{j+1}^T, dP_{j+1}^T from slot j+1, then accumulates dQ^T += K_j^T dS_j^T.  As in
+// the dK/dV kernel every wave runs every tile (the causal mask zeroes what lies past its queries)
+// and the loop is unrolled by four.  Each wave first forms rowsum(dO*O) of its 32 queries from the
+// dO fragments it holds and O read in the same layout, and stores it for the dK/dV kernel.
+// Sequence length: a multiple of 64.
+template <int HD>
+__global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dq_pipe_kernel(
+    const bf16* __restrict__ qkv, const bf16* __restrict__ out, const bf16* __restrict__ dout,
+    const float* __restrict__ lse2, float* __restrict__ dq_sum, bf16* __restrict__ dqkv, int Tn,
+    int H, float sl2, float scale) {
+  constexpr int BK = 32, NSLOT = 4, TS = BK * HD;
+  __shared__ __attribute__((aligned(16))) bf16 lds_all[NSLOT * 2 * TS];
+  SwOffsets<HD> so;
+  so.init(threadIdx.x % WAVE);
+  const int D = H * HD;
+  const long long ld = 3LL * D;
+  // grid (H*B, query blocks): the heaviest query block of every head is dispatched first
+  const int qb = gridDim.y - 1 - blockIdx.y, h = blockIdx.x % H, b = blockIdx.x / H;
+  const int lane = threadIdx.x % WAVE, w = wave_id(), lr = lane % 32, g = lane / 32;
+  const int q0 = qb * 128 + w * 32, q = q0 + lr;
+  const bf16* base = qkv + (long long)b * Tn * ld;
+  const long long srow = ((long long)b * H + h) * Tn;  // statistics row of this (batch, head)
+
+  bf16x8 qf[HD / 16], of[HD / 16];
+  float lq, dsum;
+  {
+    const int qq = min(q, Tn - 1);
+    const long long orow = ((long long)b * Tn + qq) * D + h * HD;
+    float part = 0.f;
+#pragma unroll
+    for (int c = 0; c < HD / 16; ++c) {
+      qf[c] = load8(base + (long long)qq * ld + h * HD + c * 16 + g * 8);
+      of[c] = load8(dout + orow + c * 16 + g * 8);
+      const bf16x8 o8 = load8(out + orow + c * 16 + g * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf((float)of[c][e], (float)o8[e], part);
+    }
+    dsum = part + __shfl_xor(part, 32, WAVE);  // lanes l and l^32 hold the two halves of a row
+    lq = lse2[srow + qq];
+    if (g == 0 && q < Tn) dq_sum[srow + q] = dsum;
+  }
+  f32x16 dq[HD / 32];
+#pragma unroll
+  for (int i = 0; i < HD / 32; ++i) dq[i] = f32x16{};
+
+  // waves 0-1 stage K, waves 2-3 V
+  const bool is_v = w >= 2;
+  RowStage<bf16, BK, HD, 128> st;
+  st.init(threadIdx.x % 128);
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(base + (is_v ? 2 * D : D) + h * HD, span_bytes<bf16>(Tn, ld, HD));
+  auto fetch = [&](int t) { st.load(rs, ld, t * BK, Tn); };
+  auto put = [&](int slot) { st.store(lds_all + slot * 2 * TS + (is_v ? TS : 0)); };
+
+  // S^T = K Q^T and dP^T = V dO^T of the tile in slot SL (32 keys x 32 queries)
+  auto stage_a = [&](auto sl_c, f32x16& sa, f32x16& da) {
+    const bf16* K_ = lds_all + decltype(sl_c)::value * 2 * TS;
+    const bf16* V_ = K_ + TS;
+    sa = f32x16{};
+    da = f32x16{};
+#pragma unroll
+    for (int c = 0; c < HD / 16; ++c) {
+      mma<bf16>(sa, frag_row_sw<HD>(K_, so, 0, c), qf[c]);
+      mma<bf16>(da, frag_row_sw<HD>(V_, so, 0, c), of[c]);
+    }
+  };
+  // dS^T = P^T (dP^T - rowsum(dO*O)) with P = 2^(S sl2 - LSE2) causally masked; register r holds
+  // key (r/4)*8 + g*4 + r%4 of the tile
+  auto stage_b = [&](int t, f32x16& sa, f32x16& da, bf16x8 (&sf)[2]) {
+    const int qk = q - t * BK - g * 4;  // query - first key of the lane's rows
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = fast_exp2(fmaf(sa[r], sl2, -lq));
+      if ((r / 4) * 8 + (r % 4) > qk) p = 0.f;
+      da[r] = p * (da[r] - dsum);
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) sf[hh] = acc_frag<bf16>(da, hh);
+  };
+  // dQ^T += K^T dS^T for the tile in slot SL
+  auto stage_c = [&](auto sl_c, const bf16x8 (&sf)[2]) {
+    const bf16* K_ = lds_all + decltype(sl_c)::value * 2 * TS;
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) mma<bf16>(dq[dt], frag_tr_sw<HD>(K_, so, hh * 16, dt), sf[hh]);
+  };
+
+  const int nk = min(Tn, (qb + 1) * 128) / BK;  // even
+  fetch(0);
+  put(0);
+#pragma unroll
+  for (int t = 1; t < 3; ++t)
+    if (t < nk) {
+      fetch(t);
+      put(t);
+    }
+  if (3 < nk) fetch(3);
+  __syncthreads();
+
+  auto iter = [&](auto sl_c, auto has_a_c, int j, f32x16& sc, f32x16& dc, f32x16& sn,
+                  f32x16& dn) {
+    constexpr int SL = decltype(sl_c)::value;
+    constexpr bool HAS_A = decltype(has_a_c)::value;
+    if (j + 3 < nk) put((SL + 3) % NSLOT);
+    if (j + 4 < nk) fetch(j + 4);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 sf[2];
+    stage_b(j, sc, dc, sf);
+    if constexpr (HAS_A) stage_a(std::integral_constant<int, (SL + 1) % NSLOT>(), sn, dn);
+    stage_c(sl_c, sf);
+    if constexpr (HAS_A) pipe_schedule<2 * (HD / 16), 2 * (HD / 32), 4>();
+    __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using YES = std::true_type;
+  using NO = std::false_type;
+  f32x16 s0, d0, s1, d1;
+  stage_a(I0(), s0, d0);
+  int j = 0;
+  for (; j + 4 < nk; j += 4) {
+    iter(I0(), YES(), j, s0, d0, s1, d1);
+    iter(I1(), YES(), j + 1, s1, d1, s0, d0);
+    iter(I2(), YES(), j + 2, s0, d0, s1, d1);
+    iter(I3(), YES(), j + 3, s1, d1, s0, d0);
+  }
+  if (nk - j == 4) {
+    iter(I0(), YES(), j, s0, d0, s1, d1);
+    iter(I1(), YES(), j + 1, s1, d1, s0, d0);
+    iter(I2(), YES(), j + 2, s0, d0, s1, d1);
+    iter(I3(), NO(), j + 3, s1, d1, s0, d0);
+  } else {
+    iter(I0(), YES(), j, s0, d0, s1, d1);
+    iter(I1(), NO(), j + 1, s1, d1, s0, d0);
+  }
+  if (q0 >= Tn) return;
+  store_acc_rows<bf16, HD>(dqkv + ((long long)b * Tn + q) * ld + h * HD, dq, scale, g);
 }
 
 // dQ for 128 queries per workgroup (4 waves x 32), looping over 64-key tiles double buffered in
@@ -934,21 +1078,26 @@ gpt_status launch_attn_bwd_stage(int stage, const T* qkv, const T* out, const T*
   const float scale = 1.f / sqrtf((float)hd);
   const long long N = (long long)B * Tn;
   dim3 grid(H * B, cdiv(Tn, 128));
+  if (stage != 0 && stage != 1) return fail(GPT_EINVAL, "attention backward stage must be 0 or 1");
   gpt_status st = dispatch_hd<T>(hd, [&](auto HD) {
     constexpr int hdv = decltype(HD)::value;
-    if (stage == 0)
-      attn_bwd_pre_kernel<T, hdv><<<cdiv(N * H, 256), 256, 0, s>>>(out, dout, dq_sum, N, Tn, H);
-    else if (stage == 1) {
-      if constexpr (std::is_same<T, bf16>::value)
+    if constexpr (std::is_same<T, bf16>::value) {
+      if (stage == 0)
+        attn_bwd_dq_pipe_kernel<hdv><<<grid, ATHREADS, 0, s>>>(qkv, out, dout, lse2, dq_sum, dqkv,
+                                                               Tn, H, sl2, scale);
+      else
         attn_bwd_dkdv_pipe_kernel<hdv><<<grid, ATHREADS, 0, s>>>(qkv, dout, lse2, dq_sum, dqkv, Tn,
                                                                  H, sl2, scale);
-      else
+    } else {
+      if (stage == 0) {
+        attn_bwd_pre_kernel<T, hdv><<<cdiv(N * H, 256), 256, 0, s>>>(out, dout, dq_sum, N, Tn, H);
+        attn_bwd_dq_kernel<T, hdv><<<grid, ATHREADS, 0, s>>>(qkv, dout, lse2, dq_sum, dqkv, Tn, H,
+                                                             sl2, scale);
+      } else {
         attn_bwd_dkdv_kernel<T, hdv><<<grid, ATHREADS, 0, s>>>(qkv, dout, lse2, dq_sum, dqkv, Tn,
                                                                H, sl2, scale);
+      }
     }
-    else
-      attn_bwd_dq_kernel<T, hdv><<<grid, ATHREADS, 0, s>>>(qkv, dout, lse2, dq_sum, dqkv, Tn, H,
-                                                           sl2, scale);
   });
   return st != GPT_OK ? st : check_launch("attention bwd");
 }
@@ -956,7 +1105,7 @@ gpt_status launch_attn_bwd_stage(int stage, const T* qkv, const T* out, const T*
 template <typename T>
 gpt_status launch_attn_bwd(const T* qkv, const T* out, const T* dout, const float* lse2,
                            float* dq_sum, T* dqkv, int B, int Tn, int H, int hd, hipStream_t s) {
-  for (int stage = 0; stage < 3; ++stage) {
+  for (int stage = 0; stage < 2; ++stage) {
     gpt_status st = launch_attn_bwd_stage<T>(stage, qkv, out, dout, lse2, dq_sum, dqkv, B, Tn, H,
                                              hd, s);
     if (st != GPT_OK) return st;

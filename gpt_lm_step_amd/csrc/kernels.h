@@ -70,7 +70,7 @@ gpt_status launch_loss_reduce(const float* loss_rows, long long N, const int* n_
 template <typename T>
 gpt_status launch_attn_fwd(const T* qkv, T* out, float* lse2, int B, int Tn, int H, int hd,
                            hipStream_t s);
-// stage 0: rowsum(dO * O); 1: dK, dV; 2: dQ.
+// stage 0: rowsum(dO * O) into dq_sum and dQ; stage 1: dK, dV (reads dq_sum).
 template <typename T>
 gpt_status launch_attn_bwd_stage(int stage, const T* qkv, const T* out, const T* dout,
                                  const float* lse2, float* dq_sum, T* dqkv, int B, int Tn, int H,

@@ -342,12 +342,10 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
           gemm_wgrad<G_OUT_WGRAD, T>(false, false, D, D, (int)N, dx_t, D, o, D,
                                      EpiStoreF32{G + Ly.wo[l], D, beta}, p.splitk,
                                      p.splitk_floats, s));
-    STAGE("attn_bwd_pre", 0, 2.0 * ND * es + 4.0 * N * H,
+    STAGE("attn_bwd_dq", 2.0 * pairs * hd, 0,
           launch_attn_bwd_stage<T>(0, qkv, o, dO, b.lse, p.dqsum, dqkv, Bn, Tn, H, hd, s));
     STAGE("attn_bwd_dkdv", 8.0 * pairs * hd, 0,
           launch_attn_bwd_stage<T>(1, qkv, o, dO, b.lse, p.dqsum, dqkv, Bn, Tn, H, hd, s));
-    STAGE("attn_bwd_dq", 2.0 * pairs * hd, 0,
-          launch_attn_bwd_stage<T>(2, qkv, o, dO, b.lse, p.dqsum, dqkv, Bn, Tn, H, hd, s));
     STAGE("rope_qknorm_bwd", 0, 6.0 * ND * es + 8.0 * N * H,
           launch_rope_qknorm_bwd<T>(dqkv, qkv, cos_t, sin_t, b.rstd_qk, N, Tn, H, hd, c.qk_norm, s));
     if (vadd)
