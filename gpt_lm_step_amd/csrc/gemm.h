@@ -48,14 +48,41 @@ __device__ __forceinline__ void load4(const T* p, float (&v)[4]) {
   for (int i = 0; i < 4; ++i) v[i] = to_f32(x[i]);
 }
 
+// Each epilogue is split into load(r, c), which fetches what the output depends on besides the
+// accumulator (nothing for plain stores), and store(r, c, v, pre).  The tiled kernels issue the
+// loads of all their row passes before the first store, so the load latencies overlap instead of
+// being paid one after another (the compiler cannot reorder a load after a store that may
+// alias it).  operator() is the two in sequence.
+struct NoPre {};
+template <typename T>
+struct Pre4 {
+  vec4t<T> x;
+};
+template <typename T>
+__device__ __forceinline__ Pre4<T> pre_load(const T* p) {
+  return Pre4<T>{*reinterpret_cast<const vec4t<T>*>(p)};
+}
+template <typename T>
+__device__ __forceinline__ void pre_add(const Pre4<T>& a, float (&o)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] += to_f32(a.x[i]);
+}
+#define GPT_EPI_CALL                                                                     \
+  __device__ __forceinline__ void operator()(int r, int c, const float (&v)[4]) const { \
+    store(r, c, v, load(r, c));                                                          \
+  }
+
 // out = T(acc)
 template <typename T>
 struct EpiStore {
   T* out;
   long long ldo;
-  __device__ __forceinline__ void operator()(int r, int c, const float (&v)[4]) const {
+  using Pre = NoPre;
+  __device__ __forceinline__ Pre load(int, int) const { return {}; }
+  __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre&) const {
     store4(out + (long long)r * ldo + c, v);
   }
+  GPT_EPI_CALL
 };
 
 // out = acc, or out += acc when beta != 0 (fp32 gradients, accumulation across calls).
@@ -63,17 +90,16 @@ struct EpiStoreF32 {
   float* out;
   long long ldo;
   int beta;
-  __device__ __forceinline__ void operator()(int r, int c, const float (&v)[4]) const {
-    float* p = out + (long long)r * ldo + c;
-    float o[4] = {v[0], v[1], v[2], v[3]};
-    if (beta) {
-      float old[4];
-      load4(p, old);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] += old[i];
-    }
-    store4(p, o);
+  using Pre = Pre4<float>;
+  __device__ __forceinline__ Pre load(int r, int c) const {
+    return beta ? pre_load(out + (long long)r * ldo + c) : Pre{f32x4{}};
   }
+  __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre& a) const {
+    float o[4] = {v[0], v[1], v[2], v[3]};
+    if (beta) pre_add(a, o);
+    store4(out + (long long)r * ldo + c, o);
+  }
+  GPT_EPI_CALL
 };
 
 // Split-K partial: split blockIdx.y of the K range writes its fp32 [M][N] sum at
@@ -81,11 +107,12 @@ struct EpiStoreF32 {
 struct EpiSplit {
   float* ws;
   long long stride, ldo;
-  __device__ __forceinline__ void operator()(int r, int c, const float (&v)[4]) const {
-    float* p = ws + blockIdx.y * stride + (long long)r * ldo + c;
-    const float o[4] = {v[0], v[1], v[2], v[3]};
-    store4(p, o);
+  using Pre = NoPre;
+  __device__ __forceinline__ Pre load(int, int) const { return {}; }
+  __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre&) const {
+    store4(ws + blockIdx.y * stride + (long long)r * ldo + c, v);
   }
+  GPT_EPI_CALL
 };
 
 // out = res + acc (fp32 residual stream; out may equal res).
@@ -93,14 +120,16 @@ struct EpiResid {
   const float* res;
   float* out;
   long long ld;
-  __device__ __forceinline__ void operator()(int r, int c, const float (&v)[4]) const {
-    const long long i = (long long)r * ld + c;
-    float o[4];
-    load4(res + i, o);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] += v[k];
-    store4(out + i, o);
+  using Pre = Pre4<float>;
+  __device__ __forceinline__ Pre load(int r, int c) const {
+    return pre_load(res + (long long)r * ld + c);
   }
+  __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre& a) const {
+    float o[4] = {v[0], v[1], v[2], v[3]};
+    pre_add(a, o);
+    store4(out + (long long)r * ld + c, o);
+  }
+  GPT_EPI_CALL
 };
 
 // q/k/v projection: columns >= vcol0 (the values) get the per-token addend u (fp32).
@@ -111,16 +140,17 @@ struct EpiQKV {
   const float* u;
   long long ldu;
   int vcol0;
-  __device__ __forceinline__ void operator()(int r, int c, const float (&v)[4]) const {
+  using Pre = Pre4<float>;
+  __device__ __forceinline__ Pre load(int r, int c) const {
+    // columns left of vcol0 read the row's first addend entries and ignore them
+    return u ? pre_load(u + (long long)r * ldu + max(c - vcol0, 0)) : Pre{f32x4{}};
+  }
+  __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre& a) const {
     float o[4] = {v[0], v[1], v[2], v[3]};
-    if (u && c >= vcol0) {
-      float a[4];
-      load4(u + (long long)r * ldu + (c - vcol0), a);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) o[k] += a[k];
-    }
+    if (u && c >= vcol0) pre_add(a, o);
     store4(out + (long long)r * ldo + c, o);
   }
+  GPT_EPI_CALL
 };
 
 // MLP up projection: hp = acc, act = relu(acc)^2.
@@ -129,7 +159,9 @@ struct EpiRelu2 {
   T* hp;
   T* act;
   long long ld;
-  __device__ __forceinline__ void operator()(int r, int c, const float (&v)[4]) const {
+  using Pre = NoPre;
+  __device__ __forceinline__ Pre load(int, int) const { return {}; }
+  __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre&) const {
     const long long i = (long long)r * ld + c;
     float a[4];
 #pragma unroll
@@ -140,6 +172,7 @@ struct EpiRelu2 {
     store4(hp + i, v);
     store4(act + i, a);
   }
+  GPT_EPI_CALL
 };
 
 // Down-projection input gradient through ReLU^2: out = acc * 2 * relu(hp).
@@ -148,14 +181,20 @@ struct EpiDRelu2 {
   const T* hp;
   T* out;
   long long ld;
-  __device__ __forceinline__ void operator()(int r, int c, const float (&v)[4]) const {
-    const long long i = (long long)r * ld + c;
-    float h[4], o[4];
-    load4(hp + i, h);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = h[k] > 0.f ? 2.f * h[k] * v[k] : 0.f;
-    store4(out + i, o);
+  using Pre = Pre4<T>;
+  __device__ __forceinline__ Pre load(int r, int c) const {
+    return pre_load(hp + (long long)r * ld + c);
   }
+  __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre& a) const {
+    float o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float h = to_f32(a.x[k]);
+      o[k] = h > 0.f ? 2.f * h * v[k] : 0.f;
+    }
+    store4(out + (long long)r * ld + c, o);
+  }
+  GPT_EPI_CALL
 };
 
 // out (fp32) = acc + add (add in T, optional): the value addend u = v_add + tri * wtri^T.
@@ -164,18 +203,18 @@ struct EpiAddRows {
   const T* add;
   float* out;
   long long ld;
-  __device__ __forceinline__ void operator()(int r, int c, const float (&v)[4]) const {
-    const long long i = (long long)r * ld + c;
-    float o[4] = {v[0], v[1], v[2], v[3]};
-    if (add) {
-      float a[4];
-      load4(add + i, a);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) o[k] += a[k];
-    }
-    store4(out + i, o);
+  using Pre = Pre4<T>;
+  __device__ __forceinline__ Pre load(int r, int c) const {
+    return add ? pre_load(add + (long long)r * ld + c) : Pre{vec4t<T>{}};
   }
+  __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre& a) const {
+    float o[4] = {v[0], v[1], v[2], v[3]};
+    if (add) pre_add(a, o);
+    store4(out + (long long)r * ld + c, o);
+  }
+  GPT_EPI_CALL
 };
+#undef GPT_EPI_CALL
 
 // Call sites of the GEMM: each gets its own kernel symbol, so profiles name the projection.
 enum GemmSite {
@@ -607,15 +646,24 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
                            acc[i][j][q * 4 + 3]};
           *reinterpret_cast<f32x4*>(ep + lr * EP + j * 32 + q * 8 + lg * 4) = v;
         }
-      constexpr int LPR = WTN / 4, RPP = WAVE / LPR;
+      // all passes' epilogue loads first (at in-range addresses, no per-lane branches), then
+      // the stores
+      constexpr int LPR = WTN / 4, RPP = WAVE / LPR, NP = 32 / RPP;
+      typename Epi::Pre pre[NP];
+      const int c4 = (lane % LPR) * 4, col = n0 + wn + c4;
 #pragma unroll
-      for (int rr = 0; rr < 32; rr += RPP) {
-        const int r = rr + lane / LPR, c4 = (lane % LPR) * 4;
+      for (int p = 0; p < NP; ++p) {
+        const int row = m0 + wm + i * 32 + p * RPP + lane / LPR;
+        pre[p] = epi.load(min(row, M - 1), min(col, N - 4));
+      }
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int r = p * RPP + lane / LPR;
         const f32x4 x = *reinterpret_cast<const f32x4*>(ep + r * EP + c4);
-        const int row = m0 + wm + i * 32 + r, col = n0 + wn + c4;
+        const int row = m0 + wm + i * 32 + r;
         if (row < M && col < N) {
           const float v[4] = {x[0], x[1], x[2], x[3]};
-          epi(row, col, v);
+          epi.store(row, col, v, pre[p]);
         }
       }
     }
