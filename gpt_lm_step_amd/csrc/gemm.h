@@ -85,18 +85,33 @@ struct EpiStore {
   GPT_EPI_CALL
 };
 
-// out = acc, or out += acc when beta != 0 (fp32 gradients, accumulation across calls).
+// fp32 output descriptor: out = acc, or out += acc when beta != 0 (gradients accumulated across
+// calls).  gemm() launches it as EpiPutF32 or EpiAccF32, so no kernel branches on beta.
 struct EpiStoreF32 {
   float* out;
   long long ldo;
   int beta;
+};
+struct EpiPutF32 {
+  float* out;
+  long long ldo;
+  using Pre = NoPre;
+  __device__ __forceinline__ Pre load(int, int) const { return {}; }
+  __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre&) const {
+    store4(out + (long long)r * ldo + c, v);
+  }
+  GPT_EPI_CALL
+};
+struct EpiAccF32 {
+  float* out;
+  long long ldo;
   using Pre = Pre4<float>;
   __device__ __forceinline__ Pre load(int r, int c) const {
-    return beta ? pre_load(out + (long long)r * ldo + c) : Pre{f32x4{}};
+    return pre_load(out + (long long)r * ldo + c);
   }
   __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre& a) const {
     float o[4] = {v[0], v[1], v[2], v[3]};
-    if (beta) pre_add(a, o);
+    pre_add(a, o);
     store4(out + (long long)r * ldo + c, o);
   }
   GPT_EPI_CALL
@@ -132,7 +147,8 @@ struct EpiResid {
   GPT_EPI_CALL
 };
 
-// q/k/v projection: columns >= vcol0 (the values) get the per-token addend u (fp32).
+// q/k/v projection: columns >= vcol0 (the values) get the per-token addend u (fp32).  gemm()
+// launches a plain EpiStore when u is null.
 template <typename T>
 struct EpiQKV {
   T* out;
@@ -143,11 +159,11 @@ struct EpiQKV {
   using Pre = Pre4<float>;
   __device__ __forceinline__ Pre load(int r, int c) const {
     // columns left of vcol0 read the row's first addend entries and ignore them
-    return u ? pre_load(u + (long long)r * ldu + max(c - vcol0, 0)) : Pre{f32x4{}};
+    return pre_load(u + (long long)r * ldu + max(c - vcol0, 0));
   }
   __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre& a) const {
     float o[4] = {v[0], v[1], v[2], v[3]};
-    if (u && c >= vcol0) pre_add(a, o);
+    if (c >= vcol0) pre_add(a, o);
     store4(out + (long long)r * ldo + c, o);
   }
   GPT_EPI_CALL
@@ -197,7 +213,8 @@ struct EpiDRelu2 {
   GPT_EPI_CALL
 };
 
-// out (fp32) = acc + add (add in T, optional): the value addend u = v_add + tri * wtri^T.
+// out (fp32) = acc + add (add in T, optional: gemm() launches EpiPutF32 when it is null): the
+// value addend u = v_add + tri * wtri^T.
 template <typename T>
 struct EpiAddRows {
   const T* add;
@@ -205,11 +222,11 @@ struct EpiAddRows {
   long long ld;
   using Pre = Pre4<T>;
   __device__ __forceinline__ Pre load(int r, int c) const {
-    return add ? pre_load(add + (long long)r * ld + c) : Pre{vec4t<T>{}};
+    return pre_load(add + (long long)r * ld + c);
   }
   __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre& a) const {
     float o[4] = {v[0], v[1], v[2], v[3]};
-    if (add) pre_add(a, o);
+    pre_add(a, o);
     store4(out + (long long)r * ld + c, o);
   }
   GPT_EPI_CALL
@@ -469,38 +486,42 @@ __global__ __launch_bounds__(THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_
 // Operand tiles travel global -> LDS by buffer loads that write LDS directly (16 B per lane,
 // 1 KB per wave instruction, lane l to byte 16*l of the instruction's LDS block), in the
 // operand's own global layout, so no staging registers and no LDS store instructions are used:
-//  * K-contiguous tile: [ROWS][64] bf16, 128 B rows, 16 B chunk c of row r at chunk position
-//    c ^ ((r >> 1) & 7) (fragment reads of 16 rows hit 16 distinct bank groups);
-//  * row-contiguous tile: [64 k][ROWS] bf16, chunk c of k-row k at c ^ (4 * (k % 4)); its MFMA
+//  * K-contiguous tile: [ROWS][BK] bf16; 16 B chunk c of row r at chunk position c ^ kswz(r),
+//    so that the 16 lanes of a fragment read that the LDS serves together hit 16 distinct
+//    16-byte bank groups (64 banks of 4 bytes);
+//  * row-contiguous tile: [BK k][ROWS] bf16, chunk c of k-row k at c ^ (4 * (k % 4)); its MFMA
 //    fragments come from two transposing LDS reads (ds_read_b64_tr_b16: within a 16-lane
 //    group, lane j receives element j%4 of lanes j/4 + 4i, i = 0..3; lane 4i + t addresses
 //    row k0 + i, columns n0 + 4t .. +3, so lane j gets B[k0 .. k0+3][n0 + j]).
-// Loads past the operand's end read as zeros (buffer range check).  Two LDS stages: the DMA of
-// tile kt+1 runs during the MFMAs of tile kt and is waited for at the barrier.
+// Loads past the operand's end read as zeros (buffer range check).
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
-template <int ROWS, bool KC, int NW>
+template <int ROWS, int BK, bool KC, int NW>
 struct DmaTile {
-  static constexpr int BYTES = ROWS * 64 * 2;
+  static_assert(BK == 32 || BK == 64, "K tile of 32 or 64");
+  static constexpr int BYTES = ROWS * BK * 2;
   static constexpr int NI = BYTES / 1024 / NW;          // DMA instructions per wave (NW waves)
   static_assert(NI * NW * 1024 == BYTES, "tile must split evenly over the waves");
-  // issue this wave's DMA instructions [i0, i1) for the tile at (row0, k0)
+  static constexpr int CPR = BK / 8, RPI = 64 / CPR;   // KC: chunks per row, rows per instruction
+  static __device__ __forceinline__ int kswz(int r) { return BK == 64 ? (r >> 1) & 7 : (r >> 2) & 3; }
+  // issue this wave's DMA instructions for the tile at (row0, k0)
   static __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, long long ld, int row0,
-                                               int k0, int rows_lim, int k_lim, bf16* tile,
-                                               int i0 = 0, int i1 = NI) {
+                                               int k0, int rows_lim, int k_lim, bf16* tile) {
     const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE;
 #pragma unroll
-    for (int i = i0; i < i1; ++i) {
+    for (int i = 0; i < NI; ++i) {
       const int blk = w * NI + i;  // 1 KB block of the tile
       uint32_t off;
       if constexpr (KC) {
-        const int r = blk * 8 + lane / 8, c = (lane % 8) ^ ((r >> 1) & 7);
+        const int r = blk * RPI + lane / CPR, c = (lane % CPR) ^ kswz(r);
         const int row = row0 + r, k = k0 + c * 8;
         off = (row < rows_lim && k < k_lim) ? (uint32_t)(((long long)row * ld + k) * 2) : OOB;
       } else {
-        constexpr int CPR = ROWS / 8, KPI = 1024 / (ROWS * 2);  // chunks per k-row, k-rows per block
-        const int kk = blk * KPI + lane / CPR, c = (lane % CPR) ^ (4 * (kk % 4));
+        constexpr int CPK = ROWS / 8, KPI = 1024 / (ROWS * 2);  // chunks per k-row, k-rows per block
+        const int kk = blk * KPI + lane / CPK, c = (lane % CPK) ^ (4 * (kk % 4));
         const int row = row0 + c * 8, k = k0 + kk;
         off = (row < rows_lim && k < k_lim) ? (uint32_t)(((long long)k * ld + row) * 2) : OOB;
       }
@@ -512,7 +533,7 @@ struct DmaTile {
     const int g = (lane / 32) % 2;
     if constexpr (KC) {
       const int c = ks / 8 + g;
-      return load8(tile + r * 64 + ((c ^ ((r >> 1) & 7)) * 8));
+      return load8(tile + r * BK + ((c ^ kswz(r)) * 8));
     } else {
       // r = rowbase + lane % 32; the 16-lane group of this lane covers rows nb .. nb+15
       const int j = lane % 16, i = j / 4, t = j % 4;
@@ -534,12 +555,40 @@ struct DmaTile {
   }
 };
 
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), unrolled
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>()), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>());
+}
+
+// Stage S of a kernel's LDS ring: an array of its own, so the compiler can tell the LDS reads of
+// one stage from DMA writes still in flight into another (reads of an array that a DMA may be
+// writing make it wait for all outstanding DMA).
+template <int S, int BYTES>
+__device__ __forceinline__ bf16* lds_stage() {
+  __shared__ __attribute__((aligned(1024))) bf16 buf[BYTES / 2];
+  return buf;
+}
+// Wait until at most N vector-memory operations of this wave are outstanding and all its LDS
+// operations are done (s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+}
+
 // BM x BN tile per workgroup of WGM x WGN waves; each wave computes (BM/WGM) x (BN/WGN) as
-// 32 x 32 MFMA tiles.  The 256 x 256 tile runs 8 waves, two per SIMD, so that one wave's MFMAs
-// cover the other's wait for its DMA at the barrier (with one wave per SIMD the operand
-// transfers and the MFMAs do not overlap); the 128 x 128 tile runs 4 waves, two workgroups
-// per CU.
-template <int BM, int BN, int WGM, int WGN, bool A_KC, bool B_KC, class Epi, int SITE>
+// 32 x 32 MFMA tiles.  K advances in BK-wide tiles through a ring of NS LDS stages: the DMA of
+// tile kt + NS - 1 is issued while tile kt is multiplied, so NS - 1 tiles of loads are in flight
+// behind the MFMAs.  One barrier per K tile (after this wave's DMA of tile kt has landed, so all
+// waves' have; the stage read in the previous iteration is then free for the next DMA).  The
+// 256 x 256 tile runs 8 waves, two per SIMD; the 128 x 128 tile 4 waves, two workgroups per CU.
+template <int BM, int BN, int WGM, int WGN, int BK, int NS, bool A_KC, bool B_KC, class Epi,
+          int SITE>
 __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_dma_kernel(
     const bf16* A, long long lda, const bf16* B, long long ldb, int M,
     int N, int K, uint32_t a_bytes, uint32_t b_bytes, Epi epi, int kps) {
@@ -551,10 +600,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
     B += B_KC ? (long long)k0 : (long long)k0 * ldb;
     K = min(K - k0, kps);
   }
-  constexpr int TM = WTM / 32, TN = WTN / 32, BK = 64;
-  using TA = DmaTile<BM, A_KC, NW>;
-  using TB = DmaTile<BN, B_KC, NW>;
-  __shared__ __attribute__((aligned(1024))) bf16 lds[2][(BM + BN) * BK];
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  using TA = DmaTile<BM, BK, A_KC, NW>;
+  using TB = DmaTile<BN, BK, B_KC, NW>;
+  constexpr int STAGE_BYTES = (BM + BN) * BK * 2, PER_TILE = TA::NI + TB::NI;
+  static_assert(NS >= 2 && (NS - 2) * PER_TILE < 64, "pipeline depth");
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
@@ -570,72 +620,63 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
   const int nk = (K + BK - 1) / BK;
-  TA::issue(ra, lda, m0, 0, M, K, lds[0]);
-  TB::issue(rb, ldb, n0, 0, N, K, lds[0] + BM * BK);
-  __syncthreads();  // waits for this wave's DMA, then all waves'
-
-  // The compiler cannot tell a transposing LDS read from the tile that an LDS-DMA in flight
-  // is writing, so it waits for all outstanding DMA before such a read.  A row-contiguous
-  // operand's fragments are therefore all read before the next tile's DMA is issued; a
-  // K-contiguous operand's fragments are read slice by slice, those of slice s+1 during the
-  // MFMAs of slice s.
-  constexpr bool AF = !A_KC, BF = !B_KC;                   // operands read whole, first
-  constexpr int NSA = AF ? BK / 16 : 2, NSB = BF ? BK / 16 : 2;  // fragment slots
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bf16* As = lds[cur];
-    const bf16* Bs = lds[cur] + BM * BK;
-    bf16x8 af[NSA][TM], bfr[NSB][TN];
-    auto read_a = [&](int ks, int slot) {
+  // DMA of K tile kt into stage S (branch-free: tiles past K read zeros and are never used)
+  auto issue = [&](auto s_c, int kt) {
+    TA::issue(ra, lda, m0, kt * BK, M, K, lds_stage<decltype(s_c)::value, BM * BK * 2>());
+    TB::issue(rb, ldb, n0, kt * BK, N, K, lds_stage<NS + decltype(s_c)::value, BN * BK * 2>());
+  };
+  // MFMAs of the tile in stage S; the fragments of the next 16-wide K slice are read while the
+  // current slice's MFMAs run
+  auto compute = [&](auto s_c) {
+    const bf16* As = lds_stage<decltype(s_c)::value, BM * BK * 2>();
+    const bf16* Bs = lds_stage<NS + decltype(s_c)::value, BN * BK * 2>();
+    bf16x8 af[2][TM], bfr[2][TN];
+    auto read = [&](int ks, int slot) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) af[slot][i] = TA::frag(As, wm + i * 32 + lr, ks, lane);
-    };
-    auto read_b = [&](int ks, int slot) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) bfr[slot][j] = TB::frag(Bs, wn + j * 32 + lr, ks, lane);
     };
-    // Branch-free: after the last tile the offsets fall outside K and the DMA writes zeros into
-    // the idle buffer, which nothing reads again before the final barrier.
-    auto issue_next = [&]() {
-      TA::issue(ra, lda, m0, (kt + 1) * BK, M, K, lds[cur ^ 1]);
-      TB::issue(rb, ldb, n0, (kt + 1) * BK, N, K, lds[cur ^ 1] + BM * BK);
-    };
-    if constexpr (AF) {
-#pragma unroll
-      for (int s = 0; s < NSA; ++s) read_a(s * 16, s);
-    }
-    if constexpr (BF) {
-#pragma unroll
-      for (int s = 0; s < NSB; ++s) read_b(s * 16, s);
-    }
-    issue_next();
-    if constexpr (!AF) read_a(0, 0);
-    if constexpr (!BF) read_b(0, 0);
+    read(0, 0);
 #pragma unroll
     for (int ks = 0; ks < BK; ks += 16) {
-      const int sa = AF ? ks / 16 : (ks / 16) & 1, sb = BF ? ks / 16 : (ks / 16) & 1;
-      if (!AF && ks + 16 < BK) read_a(ks + 16, sa ^ 1);
-      if (!BF && ks + 16 < BK) read_b(ks + 16, sb ^ 1);
+      const int slot = (ks / 16) & 1;
+      if (ks + 16 < BK) read(ks + 16, slot ^ 1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) Mma<bf16>::run(acc[i][j], bfr[sb][j], af[sa][i]);
+        for (int j = 0; j < TN; ++j) Mma<bf16>::run(acc[i][j], bfr[slot][j], af[slot][i]);
     }
-    // keep the barrier (and the DMA wait in front of it) behind the MFMAs, which touch no
-    // memory and would otherwise be scheduled past it
+  };
+  // iteration kt, on stage S = kt % NS
+  auto step = [&](auto s_c, int kt) {
+    constexpr int S = decltype(s_c)::value;
+    wait_vm_lds<(NS - 2) * PER_TILE>();  // this wave's DMA of tile kt has landed
+    __builtin_amdgcn_s_barrier();         // ... and every wave's; stage S - 1 is free
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-  }
+    issue(std::integral_constant<int, (S + NS - 1) % NS>(), kt + NS - 1);
+    if (kt < nk) compute(s_c);
+    // keep the next iteration's wait and barrier behind these MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  static_for<NS - 1>([&](auto s_c) { issue(s_c, decltype(s_c)::value); });
+  for (int kt = 0; kt < nk; kt += NS)
+    static_for<NS>([&](auto s_c) { step(s_c, kt + decltype(s_c)::value); });
+  // drain the DMA of the tiles past K before the epilogue reuses the stages
+  wait_vm_lds<0>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 
-  // Epilogue through LDS (free once the last K tile is consumed).  The MFMA computed each
-  // 32 x 32 tile transposed (B fragment first), so lane l holds output row l%32 and, in
-  // registers 4q..4q+3, columns q*8 + (l/32)*4 + 0..3.  Each wave writes 32-row slices of its
-  // tile to its own LDS region (row pitch WTN + 4 floats: conflict-free), then reads them back
-  // row-major so that consecutive lanes cover consecutive 4-column groups of one row.
-  {
-    constexpr int EP = WTN + 4;
-    static_assert(NW * 32 * EP * 4 <= 2 * (BM + BN) * BK * 2, "epilogue staging must fit");
-    float* ep = reinterpret_cast<float*>(&lds[0][0]) + w * 32 * EP;
+  // Epilogue through LDS.  The MFMA computed each 32 x 32 tile transposed (B fragment first), so
+  // lane l holds output row l%32 and, in registers 4q..4q+3, columns q*8 + (l/32)*4 + 0..3.  Each
+  // wave writes 32-row slices of its tile to its own 8 KB LDS region (32 rows x WTN floats, 16-byte
+  // chunk c of row r at chunk c ^ (r % 16): conflict-free for the column writes and the row
+  // reads), then reads them back row-major so that consecutive lanes cover consecutive 4-column
+  // groups of one row.  The regions lie in the A halves of the stages.
+  static_assert(WTN == 64, "epilogue staging assumes 64-column wave tiles");
+  constexpr int REGION = 32 * WTN * 4, WPA = BM * BK * 2 / REGION;
+  static_assert(WPA >= 1 && NS * WPA >= NW, "epilogue staging must fit the stages");
+  auto epilogue = [&](lds_f32* ep) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -644,7 +685,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
         for (int q = 0; q < 4; ++q) {
           const f32x4 v = {acc[i][j][q * 4], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2],
                            acc[i][j][q * 4 + 3]};
-          *reinterpret_cast<f32x4*>(ep + lr * EP + j * 32 + q * 8 + lg * 4) = v;
+          const int chunk = (j * 32 + q * 8 + lg * 4) / 4;
+          *reinterpret_cast<lds_f32x4*>(ep + lr * WTN + ((chunk ^ (lr % 16)) * 4)) = v;
         }
       // all passes' epilogue loads first (at in-range addresses, no per-lane branches), then
       // the stores
@@ -659,7 +701,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         const int r = p * RPP + lane / LPR;
-        const f32x4 x = *reinterpret_cast<const f32x4*>(ep + r * EP + c4);
+        const f32x4 x = *reinterpret_cast<const lds_f32x4*>(ep + r * WTN + (((c4 / 4) ^ (r % 16)) * 4));
         const int row = m0 + wm + i * 32 + r;
         if (row < M && col < N) {
           const float v[4] = {x[0], x[1], x[2], x[3]};
@@ -667,7 +709,35 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
         }
       }
     }
-  }
+  };
+  // the region pointer stays in the LDS address space (a generic pointer would turn the
+  // accesses into flat ones, which wait on global memory traffic too)
+  lds_f32* stages[NS];
+  static_for<NS>([&](auto s_c) {
+    stages[decltype(s_c)::value] = (lds_f32*)lds_stage<decltype(s_c)::value, BM * BK * 2>();
+  });
+  epilogue(stages[w / WPA] + (w % WPA) * (REGION / 4));
+}
+
+// Calls f with an epilogue whose loads do not depend on run-time flags: accumulate vs overwrite
+// and present vs absent addends become distinct types (a load that a flag may skip leaves the
+// kernel unable to count its outstanding loads, so it waits for all of them).
+template <class Epi, class F>
+inline void with_static_epi(const Epi& e, F&& f) { f(e); }
+template <class F>
+inline void with_static_epi(const EpiStoreF32& e, F&& f) {
+  if (e.beta) f(EpiAccF32{e.out, e.ldo});
+  else f(EpiPutF32{e.out, e.ldo});
+}
+template <typename T, class F>
+inline void with_static_epi(const EpiQKV<T>& e, F&& f) {
+  if (e.u) f(e);
+  else f(EpiStore<T>{e.out, e.ldo});
+}
+template <typename T, class F>
+inline void with_static_epi(const EpiAddRows<T>& e, F&& f) {
+  if (e.add) f(e);
+  else f(EpiPutF32{e.out, e.ld});
 }
 
 // Bytes spanned by an operand of `rows` x K (KC: rows of ld; RC: K rows of ld).
@@ -684,7 +754,7 @@ void launch_dma(bool a_kc, bool b_kc, int M, int N, int K, const bf16* A, long l
   const uint32_t ab = (uint32_t)operand_bytes(a_kc, M, kps, lda, 2);
   const uint32_t bb = (uint32_t)operand_bytes(b_kc, N, kps, ldb, 2);
 #define GEMM_DMA(AK, BK_)                                                                      \
-  gemm_dma_kernel<BM, BN, WGM, WGN, AK, BK_, Epi, SITE><<<grid, 64 * WGM * WGN, 0, s>>>(        \
+  gemm_dma_kernel<BM, BN, WGM, WGN, 32, 4, AK, BK_, Epi, SITE><<<grid, 64 * WGM * WGN, 0, s>>>( \
       A, lda, B, ldb, M, N, K, ab, bb, epi, kps)
   if (a_kc && b_kc) GEMM_DMA(true, true);
   else if (a_kc) GEMM_DMA(true, false);
@@ -732,15 +802,18 @@ inline gpt_status gemm(bool a_kc, bool b_kc, int M, int N, int K, const T* A, lo
     return fail(GPT_ESHAPE, "gemm: each operand must span at most 2 GiB");
   const long long big_tiles = (long long)cdiv(M, 256) * cdiv(N, 256);
   if ((long long)cdiv(M, 128) * cdiv(N, 128) >= (1LL << 31)) return fail(GPT_ESHAPE, "gemm: too many tiles");
-  if constexpr (std::is_same<T, bf16>::value) {
-    if (big_tiles >= 240)
-      gemm_detail::launch_dma<256, 256, 2, 4, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
-    else
-      gemm_detail::launch_dma<128, 128, 2, 2, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
-  } else {
-    // fp32 serves the small parity configurations only
-    gemm_detail::launch_tiles<T, 64, 64, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s);
-  }
+  gemm_detail::with_static_epi(epi, [&](const auto& e) {
+    using E = typename std::decay<decltype(e)>::type;
+    if constexpr (std::is_same<T, bf16>::value) {
+      if (big_tiles >= 240)
+        gemm_detail::launch_dma<256, 256, 2, 4, E, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, e, s);
+      else
+        gemm_detail::launch_dma<128, 128, 2, 2, E, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, e, s);
+    } else {
+      // fp32 serves the small parity configurations only
+      gemm_detail::launch_tiles<T, 64, 64, E, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, e, s);
+    }
+  });
   return check_launch("gemm");
 }
 
