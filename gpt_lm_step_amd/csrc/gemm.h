@@ -604,7 +604,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
   using TA = DmaTile<BM, BK, A_KC, NW>;
   using TB = DmaTile<BN, BK, B_KC, NW>;
   constexpr int STAGE_BYTES = (BM + BN) * BK * 2, PER_TILE = TA::NI + TB::NI;
-  static_assert(NS >= 2 && (NS - 2) * PER_TILE < 64, "pipeline depth");
+  static_assert(NS >= 3 && (NS - 2) * PER_TILE < 64, "pipeline depth");
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
@@ -625,33 +625,41 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
     TA::issue(ra, lda, m0, kt * BK, M, K, lds_stage<decltype(s_c)::value, BM * BK * 2>());
     TB::issue(rb, ldb, n0, kt * BK, N, K, lds_stage<NS + decltype(s_c)::value, BN * BK * 2>());
   };
-  // MFMAs of the tile in stage S; the fragments of the next 16-wide K slice are read while the
-  // current slice's MFMAs run
+  // Fragments: slot 0 holds the first 16-wide K slice of the current tile, read during the
+  // previous tile's last MFMAs (so the barrier between tiles costs no LDS latency); each slice's
+  // successor is read while its MFMAs run.
+  bf16x8 af[2][TM], bfr[2][TN];
+  auto read = [&](const bf16* As, const bf16* Bs, int ks, int slot) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[slot][i] = TA::frag(As, wm + i * 32 + lr, ks, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[slot][j] = TB::frag(Bs, wn + j * 32 + lr, ks, lane);
+  };
+  auto stage_a = [&](auto s_c) -> const bf16* {
+    return lds_stage<decltype(s_c)::value, BM * BK * 2>();
+  };
+  auto stage_b = [&](auto s_c) -> const bf16* {
+    return lds_stage<NS + decltype(s_c)::value, BN * BK * 2>();
+  };
+  // MFMAs of the tile in stage S, then slice 0 of the tile in stage S + 1
   auto compute = [&](auto s_c) {
-    const bf16* As = lds_stage<decltype(s_c)::value, BM * BK * 2>();
-    const bf16* Bs = lds_stage<NS + decltype(s_c)::value, BN * BK * 2>();
-    bf16x8 af[2][TM], bfr[2][TN];
-    auto read = [&](int ks, int slot) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[slot][i] = TA::frag(As, wm + i * 32 + lr, ks, lane);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[slot][j] = TB::frag(Bs, wn + j * 32 + lr, ks, lane);
-    };
-    read(0, 0);
+    using SN = std::integral_constant<int, (decltype(s_c)::value + 1) % NS>;
 #pragma unroll
     for (int ks = 0; ks < BK; ks += 16) {
       const int slot = (ks / 16) & 1;
-      if (ks + 16 < BK) read(ks + 16, slot ^ 1);
+      if (ks + 16 < BK) read(stage_a(s_c), stage_b(s_c), ks + 16, slot ^ 1);
+      else read(stage_a(SN()), stage_b(SN()), 0, slot ^ 1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) Mma<bf16>::run(acc[i][j], bfr[slot][j], af[slot][i]);
     }
   };
+  static_assert(BK == 32, "slot 0 must hold the first slice of every tile");
   // iteration kt, on stage S = kt % NS
   auto step = [&](auto s_c, int kt) {
     constexpr int S = decltype(s_c)::value;
-    wait_vm_lds<(NS - 2) * PER_TILE>();  // this wave's DMA of tile kt has landed
+    wait_vm_lds<(NS - 3) * PER_TILE>();  // this wave's DMA of tile kt + 1 has landed
     __builtin_amdgcn_s_barrier();         // ... and every wave's; stage S - 1 is free
     __builtin_amdgcn_sched_barrier(0);
     issue(std::integral_constant<int, (S + NS - 1) % NS>(), kt + NS - 1);
@@ -660,6 +668,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
     __builtin_amdgcn_sched_barrier(0);
   };
   static_for<NS - 1>([&](auto s_c) { issue(s_c, decltype(s_c)::value); });
+  wait_vm_lds<(NS - 2) * PER_TILE>();  // tile 0
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  read(stage_a(std::integral_constant<int, 0>()), stage_b(std::integral_constant<int, 0>()), 0, 0);
   for (int kt = 0; kt < nk; kt += NS)
     static_for<NS>([&](auto s_c) { step(s_c, kt + decltype(s_c)::value); });
   // drain the DMA of the tiles past K before the epilogue reuses the stages
