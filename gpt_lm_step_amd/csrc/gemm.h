@@ -604,7 +604,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
   using TA = DmaTile<BM, BK, A_KC, NW>;
   using TB = DmaTile<BN, BK, B_KC, NW>;
   constexpr int STAGE_BYTES = (BM + BN) * BK * 2, PER_TILE = TA::NI + TB::NI;
-  static_assert(NS >= 3 && (NS - 2) * PER_TILE < 64, "pipeline depth");
+  static_assert(NS >= 2 && (NS - 2) * PER_TILE < 64, "pipeline depth");
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
@@ -655,25 +655,77 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
         for (int j = 0; j < TN; ++j) Mma<bf16>::run(acc[i][j], bfr[slot][j], af[slot][i]);
     }
   };
-  static_assert(BK == 32, "slot 0 must hold the first slice of every tile");
-  // iteration kt, on stage S = kt % NS
-  auto step = [&](auto s_c, int kt) {
-    constexpr int S = decltype(s_c)::value;
-    wait_vm_lds<(NS - 3) * PER_TILE>();  // this wave's DMA of tile kt + 1 has landed
-    __builtin_amdgcn_s_barrier();         // ... and every wave's; stage S - 1 is free
+  static_assert(BK % 32 == 0, "slot 0 must hold the first slice of every tile");
+  constexpr int NSL = BK / 16;  // 16-wide K slices per tile
+  if constexpr (NS >= 3) {
+    // iteration kt, on stage S = kt % NS: the barrier comes first, then the DMA of tile
+    // kt + NS - 1 into the stage freed by the previous iteration
+    auto step = [&](auto s_c, int kt) {
+      constexpr int S = decltype(s_c)::value;
+      wait_vm_lds<(NS - 3) * PER_TILE>();  // this wave's DMA of tile kt + 1 has landed
+      __builtin_amdgcn_s_barrier();         // ... and every wave's; stage S - 1 is free
+      __builtin_amdgcn_sched_barrier(0);
+      issue(std::integral_constant<int, (S + NS - 1) % NS>(), kt + NS - 1);
+      if (kt < nk) compute(s_c);
+      // keep the next iteration's wait and barrier behind these MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    static_for<NS - 1>([&](auto s_c) { issue(s_c, decltype(s_c)::value); });
+    wait_vm_lds<(NS - 2) * PER_TILE>();  // tile 0
+    __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue(std::integral_constant<int, (S + NS - 1) % NS>(), kt + NS - 1);
-    if (kt < nk) compute(s_c);
-    // keep the next iteration's wait and barrier behind these MFMAs
+    read(stage_a(std::integral_constant<int, 0>()), stage_b(std::integral_constant<int, 0>()), 0, 0);
+    for (int kt = 0; kt < nk; kt += NS)
+      static_for<NS>([&](auto s_c) { step(s_c, kt + decltype(s_c)::value); });
+  } else {
+    // two stages (64-wide K tiles, so K-contiguous rows are whole 128-byte lines): iteration kt
+    // issues the DMA of tile kt + 1 into the other stage (every wave has read all of tile kt - 1
+    // before the previous barrier), multiplies slices 0 .. NSL-2, waits for that DMA and meets
+    // the other waves at the barrier, then multiplies the last slice while reading the first
+    // slice of tile kt + 1
+    static_assert(NS == 2, "two or at least three stages");
+    auto step = [&](auto s_c, int kt) {
+      constexpr int S = decltype(s_c)::value;
+      using SN = std::integral_constant<int, S ^ 1>;
+      issue(SN(), kt + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt < nk) {
+#pragma unroll
+        for (int sl = 0; sl < NSL - 1; ++sl) {
+          const int slot = sl & 1;
+          if (sl + 1 < NSL - 1) read(stage_a(s_c), stage_b(s_c), (sl + 1) * 16, slot ^ 1);
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) Mma<bf16>::run(acc[i][j], bfr[slot][j], af[slot][i]);
+        }
+        // the last slice's fragments, then the barrier (the reads have completed by then)
+        read(stage_a(s_c), stage_b(s_c), (NSL - 1) * 16, (NSL - 1) & 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm_lds<0>();               // this wave's DMA of tile kt + 1 has landed
+      __builtin_amdgcn_s_barrier();   // ... and every wave's; all reads of tile kt are done
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt < nk) {
+        constexpr int slot = (NSL - 1) & 1;
+        read(stage_a(SN()), stage_b(SN()), 0, slot ^ 1);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) Mma<bf16>::run(acc[i][j], bfr[slot][j], af[slot][i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    issue(std::integral_constant<int, 0>(), 0);
+    wait_vm_lds<0>();
+    __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-  };
-  static_for<NS - 1>([&](auto s_c) { issue(s_c, decltype(s_c)::value); });
-  wait_vm_lds<(NS - 2) * PER_TILE>();  // tile 0
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  read(stage_a(std::integral_constant<int, 0>()), stage_b(std::integral_constant<int, 0>()), 0, 0);
-  for (int kt = 0; kt < nk; kt += NS)
-    static_for<NS>([&](auto s_c) { step(s_c, kt + decltype(s_c)::value); });
+    read(stage_a(std::integral_constant<int, 0>()), stage_b(std::integral_constant<int, 0>()), 0, 0);
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(std::integral_constant<int, 0>(), kt);
+      step(std::integral_constant<int, 1>(), kt + 1);
+    }
+  }
   // drain the DMA of the tiles past K before the epilogue reuses the stages
   wait_vm_lds<0>();
   __builtin_amdgcn_s_barrier();
@@ -681,11 +733,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
 
   // Epilogue through LDS.  The MFMA computed each 32 x 32 tile transposed (B fragment first), so
   // lane l holds output row l%32 and, in registers 4q..4q+3, columns q*8 + (l/32)*4 + 0..3.  Each
-  // wave writes 32-row slices of its tile to its own 8 KB LDS region (32 rows x WTN floats, 16-byte
+  // wave writes 32-row slices of its tile to its own LDS region (32 rows x WTN floats, 16-byte
   // chunk c of row r at chunk c ^ (r % 16): conflict-free for the column writes and the row
   // reads), then reads them back row-major so that consecutive lanes cover consecutive 4-column
   // groups of one row.  The regions lie in the A halves of the stages.
-  static_assert(WTN == 64, "epilogue staging assumes 64-column wave tiles");
+  static_assert(WTN % 64 == 0, "epilogue staging assumes wave tiles of 64-column multiples");
   constexpr int REGION = 32 * WTN * 4, WPA = BM * BK * 2 / REGION;
   static_assert(WPA >= 1 && NS * WPA >= NW, "epilogue staging must fit the stages");
   auto epilogue = [&](lds_f32* ep) {
@@ -765,13 +817,16 @@ void launch_dma(bool a_kc, bool b_kc, int M, int N, int K, const bf16* A, long l
   // each split's operand spans at most these bytes from its own start
   const uint32_t ab = (uint32_t)operand_bytes(a_kc, M, kps, lda, 2);
   const uint32_t bb = (uint32_t)operand_bytes(b_kc, N, kps, ldb, 2);
-#define GEMM_DMA(AK, BK_)                                                                      \
-  gemm_dma_kernel<BM, BN, WGM, WGN, 32, 4, AK, BK_, Epi, SITE><<<grid, 64 * WGM * WGN, 0, s>>>( \
+  // A K-contiguous A reads whole 128-byte lines only with 64-wide K tiles, which leave room for
+  // two stages; with a row-contiguous A (whole lines at any depth) four 32-wide stages are used
+  // (the 64-wide two-stage form of that layout does not fit the registers)
+#define GEMM_DMA(AK, BK_, KT, NS_)                                                               \
+  gemm_dma_kernel<BM, BN, WGM, WGN, KT, NS_, AK, BK_, Epi, SITE><<<grid, 64 * WGM * WGN, 0, s>>>( \
       A, lda, B, ldb, M, N, K, ab, bb, epi, kps)
-  if (a_kc && b_kc) GEMM_DMA(true, true);
-  else if (a_kc) GEMM_DMA(true, false);
-  else if (b_kc) GEMM_DMA(false, true);
-  else GEMM_DMA(false, false);
+  if (a_kc && b_kc) GEMM_DMA(true, true, 64, 2);
+  else if (a_kc) GEMM_DMA(true, false, 64, 2);
+  else if (b_kc) GEMM_DMA(false, true, 32, 4);
+  else GEMM_DMA(false, false, 32, 4);
 #undef GEMM_DMA
 }
 
