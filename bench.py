@@ -30,7 +30,7 @@ PEAK_FP32 = 157.3e12     # MI355X fp32 (matrix and vector), FLOP/s
 PEAK_HBM = 8.0e12        # MI355X HBM3E, B/s
 METRIC = "train tokens/sec (fwd+bwd) on 1 MI355X + MFU vs bf16 MFMA peak"
 DENSE = {"d32": configs.D32, "gpt2": configs.GPT2_SMALL, "tiny": configs.TINY}
-WORKLOADS = sorted(list(DENSE) + ["tables", "speedrun"])
+WORKLOADS = sorted(list(DENSE) + ["tables", "speedrun", "copy"])
 # Stages made of several kernels (their time is not one kernel's launch duration); the weight-
 # gradient stages join them when their shape is split over K (see split_stages).
 MULTI_KERNEL = {"wte_segsum"}
@@ -53,6 +53,106 @@ def multi_stages(B, cfg):
     return split_stages(B, cfg) | extra
 
 
+# Kernels whose HBM traffic has been measured with rocprofv3 counters (profiles/traffic.json): the
+# stage name, substrings of the kernel symbol ('|'-separated alternatives: mangled or demangled)
+# that identify it in the counter output, and the source file the measurement belongs to.
+TRAFFIC_KERNELS = {
+    "down_dgrad": ("EpiDRelu2", "gemm.h"),
+    "up_fwd": ("EpiRelu2", "gemm.h"),
+    "down_fwd": ("EpiResidELi4E|EpiResid, 4>", "gemm.h"),
+    "attn_bwd_dkdv": ("attn_bwd_dkdv_pipe_kernel", "attn.hip"),
+    "bigram_fwd (hash + gather-add, x0 table)": ("bigram_gather_kernel", "tables.hip"),
+}
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gpt_lm_step_amd", "csrc")
+
+
+def _source_sha(name):
+    import hashlib
+    return hashlib.sha256(open(os.path.join(CSRC, name), "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of `stage` from the stored counter measurement, or None when there is
+    none or the kernel's source has changed since it was taken."""
+    try:
+        entries = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    for e in entries:
+        if e["workload"] == workload and e["stage"] == stage:
+            if e["source_sha"] != _source_sha(e["source"]):
+                return None
+            return e["hbm_bytes_per_launch"]
+    return None
+
+
+def _counter_per_dispatch(out_dir, counter, pattern):
+    """Mean of `counter` (summed over instances) per dispatch of the kernels matching `pattern`."""
+    import csv
+    import glob
+    import collections
+    f = glob.glob(os.path.join(out_dir, "*counter_collection.csv"))[0]
+    per = collections.defaultdict(float)
+    for r in csv.DictReader(open(f)):
+        if r["Counter_Name"] == counter and any(p in r["Kernel_Name"] for p in pattern.split("|")):
+            per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    assert per, f"no {counter} rows for {pattern} in {out_dir}"
+    return sum(per.values()) / len(per)
+
+
+def record_traffic(a):
+    """Write profiles/traffic.json entries for this workload from four rocprofv3 --pmc output
+    directories: FETCH_SIZE and WRITE_SIZE over the workload, and the same over `--workload copy`
+    (a device copy of COPY_BYTES, read once and written once), which scales each counter."""
+    fetch_dir, write_dir, copy_fetch_dir, copy_write_dir = a.record_traffic
+    copy_pat = "copyBuffer"
+    fs = COPY_BYTES / (1024.0 * _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", copy_pat))
+    ws = COPY_BYTES / (1024.0 * _counter_per_dispatch(copy_write_dir, "WRITE_SIZE", copy_pat))
+    try:
+        entries = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        entries = []
+    for stage, (pattern, source) in TRAFFIC_KERNELS.items():
+        try:
+            fk = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", pattern)
+            wk = _counter_per_dispatch(write_dir, "WRITE_SIZE", pattern)
+        except AssertionError:
+            continue
+        entries = [e for e in entries if not (e["workload"] == a.workload and e["stage"] == stage)]
+        entries.append({"workload": a.workload, "stage": stage, "kernel_pattern": pattern,
+                        "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+                        "copy_fetch_scale": round(fs, 4), "copy_write_scale": round(ws, 4),
+                        "hbm_bytes_per_launch": round(fk * 1024 * fs + wk * 1024 * ws),
+                        "source": source, "source_sha": _source_sha(source)})
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(entries, f, indent=1)
+    print(json.dumps(entries, indent=1))
+
+
+COPY_BYTES = 1 << 30
+
+
+def bench_copy(a):
+    """Calibration: a plain device-to-device copy of COPY_BYTES (read once, written once)."""
+    import torch
+    x = torch.ones(COPY_BYTES // 4, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(a.warmup):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(a.steps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    return {"metric": "device copy bytes/s (counter calibration)", "value": 2 * COPY_BYTES / ms / 1e6,
+            "unit": "MB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+            "higher_is_better": True, "config": {"workload": "copy", "bytes": COPY_BYTES}}
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -63,6 +163,9 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=384,
                     help="tokens of the CPU-oracle sample (one sequence)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--record-traffic", nargs=4, metavar="DIR",
+                    help="write profiles/traffic.json from rocprofv3 --pmc output directories: "
+                         "FETCH_SIZE and WRITE_SIZE of the workload, then of --workload copy")
     return ap.parse_args()
 
 
@@ -106,7 +209,7 @@ def _roof_entry(name, calls, tot_ms, flops, nbytes, bf16):
             "avg_launch_ms": round(per_launch_s * 1e3, 4), "algorithmic_per_launch": nbytes / calls}
 
 
-def profile_stages(B, ctx, step, n_steps, bf16, multi=frozenset()):
+def profile_stages(B, ctx, step, n_steps, bf16, multi=frozenset(), workload=None):
     """Instrumented pass: every launch bracketed by events on the step's stream.  Returns the
     dominant single-kernel stage's roofline and a per-stage table."""
     import torch
@@ -125,7 +228,7 @@ def profile_stages(B, ctx, step, n_steps, bf16, multi=frozenset()):
     single = [s for s in stages if s[0] not in MULTI_KERNEL and s[0] not in multi]
     name, calls, tot_ms, flops, nbytes = max(single, key=lambda s: s[2])
     roof = _roof_entry(name, calls, tot_ms, flops, nbytes, bf16)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(workload, name)
     roof["launches_per_step"] = calls // ps
     return roof, parts
 
@@ -165,7 +268,8 @@ def bench_dense(a, B):
     ms, wall = time_steps(step, a.steps, a.warmup)
     lval = float(loss.item())
     assert np.isfinite(lval), lval
-    roof, parts = profile_stages(B, ctx, step, a.profile_steps, bf16, multi_stages(B, cfg))
+    roof, parts = profile_stages(B, ctx, step, a.profile_steps, bf16, multi_stages(B, cfg),
+                                 a.workload)
 
     tok_s = cfg.tokens / (ms / 1e3)
     fpt = configs.flops_per_token(cfg)
@@ -297,7 +401,9 @@ def bench_tables(a, B):
     dom = "gather_x0"  # one kernel per call: its launch duration is the call's
     roof = {"bound": "hbm", "kernel": "bigram_fwd (hash + gather-add, x0 table)",
             "achieved": table[dom]["achieved"], "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-            "frac": table[dom]["frac"], "traffic": None, "launches_per_step": 1,
+            "frac": table[dom]["frac"],
+            "traffic": measured_traffic("tables", "bigram_fwd (hash + gather-add, x0 table)"),
+            "launches_per_step": 1,
             "avg_launch_ms": table[dom]["ms"], "algorithmic_per_launch": alg[dom]}
     out = {
         "metric": "hashed-table tokens/sec (gather fwd + scatter-reduce/update bwd, 2 tables) on 1 MI355X",
@@ -364,7 +470,7 @@ def bench_speedrun(a, B):
     # stages of the dense micro-batch step
     roof, parts = profile_stages(B, ctx, lambda: B.gpt_fwd_bwd(
         ctx, t_in[0], t_tg[0], params, grads, loss, 1.0 / MB, 1, add_x0, add_v, add_tri,
-        d_x0[:N], d_v[:N]), a.profile_steps, True, multi_stages(B, cfg))
+        d_x0[:N], d_v[:N]), a.profile_steps, True, multi_stages(B, cfg), a.workload)
     n_tok = MB * N
     tok_s = n_tok / (ms / 1e3)
     fpt = configs.flops_per_token(cfg)
@@ -396,6 +502,9 @@ def bench_speedrun(a, B):
 
 def main():
     a = parse()
+    if a.record_traffic:
+        record_traffic(a)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only: the step has no multi-GPU path (got --gpus {a.gpus})",
               file=sys.stderr)
@@ -408,7 +517,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    if a.workload == "tables":
+    if a.workload == "copy":
+        out = bench_copy(a)
+    elif a.workload == "tables":
         out = bench_tables(a, B)
     elif a.workload == "speedrun":
         out = bench_speedrun(a, B)
