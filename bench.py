@@ -149,7 +149,7 @@ def bench_copy(a):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / a.steps
     return {"metric": "device copy bytes/s (counter calibration)", "value": 2 * COPY_BYTES / ms / 1e6,
-            "unit": "MB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+            "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
             "higher_is_better": True, "config": {"workload": "copy", "bytes": COPY_BYTES}}
 
 

@@ -603,7 +603,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
   constexpr int TM = WTM / 32, TN = WTN / 32;
   using TA = DmaTile<BM, BK, A_KC, NW>;
   using TB = DmaTile<BN, BK, B_KC, NW>;
-  constexpr int STAGE_BYTES = (BM + BN) * BK * 2, PER_TILE = TA::NI + TB::NI;
+  constexpr int PER_TILE = TA::NI + TB::NI;  // DMA instructions per wave per K tile
   static_assert(NS >= 2 && (NS - 2) * PER_TILE < 64, "pipeline depth");
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;

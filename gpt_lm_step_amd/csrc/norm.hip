@@ -190,70 +190,46 @@ __global__ __launch_bounds__(256) void rms_bwd_kernel(
 }
 
 // ------------------------------------------------------------------ rotary + QK-norm
-// In place on the q and k column blocks of qkv [N, 3D].  One thread per 4 consecutive rotation
-// pairs (i..i+3, i+half..i+half+3) of one head: 8-byte (bf16) / 16-byte (fp32) accesses; the
-// Hd/8 lanes of a head reduce the head's sum of squares.  rstd_qk [N, 2H]: q heads then k heads.
-template <typename T>
-__device__ __forceinline__ void ld4(const T* p, float (&v)[4]) {
-  if constexpr (sizeof(T) == 2) {
-    const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (float)x[i];
-  } else {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = x[i];
-  }
-}
-template <typename T>
-__device__ __forceinline__ void st4(T* p, const float (&v)[4]) {
-  if constexpr (sizeof(T) == 2) {
-    bf16x4 x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (bf16)v[i];
-    *reinterpret_cast<bf16x4*>(p) = x;
-  } else {
-    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
-  }
-}
-
+// In place on the q and k column blocks of qkv [N, 3D].  One thread per 8 consecutive rotation
+// pairs (i..i+7, i+half..i+half+7) of one head: 16-byte (bf16) / 32-byte (fp32) accesses; the
+// Hd/16 lanes of a head reduce the head's sum of squares.  rstd_qk [N, 2H]: q heads then k heads.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_qknorm_fwd_kernel(
     T* __restrict__ qkv, const T* __restrict__ cos_t, const T* __restrict__ sin_t,
     float* __restrict__ rstd_qk, long long N, int Tn, int H, int hd, int qk_norm, float eps) {
-  const int D = H * hd, half = hd / 2, per_tok = D / 4;  // threads per token (q and k)
+  const int D = H * hd, half = hd / 2, per_tok = D / 8;  // threads per token (q and k)
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= N * per_tok) return;  // per_tok is a multiple of 16: whole lane groups exit together
+  if (gid >= N * per_tok) return;  // per_tok is a multiple of hd/16: whole lane groups exit together
   const long long tok = gid / per_tok;
-  const int p = (int)(gid % per_tok) * 4;
+  const int p = (int)(gid % per_tok) * 8;
   const int hq = p / half, i = p % half;
   const int t = (int)(tok % Tn);
   T* base = qkv + tok * 3 * D + (hq < H ? 0 : D) + (hq % H) * hd;
-  float x1[4], x2[4], c[4], sn[4], y1[4], y2[4];
-  ld4(base + i, x1);
-  ld4(base + i + half, x2);
-  ld4(cos_t + t * half + i, c);
-  ld4(sin_t + t * half + i, sn);
+  float x1[8], x2[8], c[8], sn[8], y1[8], y2[8];
+  load8_f32(base + i, x1);
+  load8_f32(base + i + half, x2);
+  load8_f32(cos_t + t * half + i, c);
+  load8_f32(sin_t + t * half + i, sn);
   float ss = 0.f;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
+  for (int e = 0; e < 8; ++e) {
     y1[e] = x1[e] * c[e] + x2[e] * sn[e];
     y2[e] = -x1[e] * sn[e] + x2[e] * c[e];
     ss += y1[e] * y1[e] + y2[e] * y2[e];
   }
   float r = 1.f;
   if (qk_norm) {
-    ss = group_sum(ss, half / 4);
+    ss = group_sum(ss, half / 8);
     r = 1.f / sqrtf(ss / (float)hd + eps);
     if (i == 0) rstd_qk[tok * 2 * H + hq] = r;
   }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
+  for (int e = 0; e < 8; ++e) {
     y1[e] *= r;
     y2[e] *= r;
   }
-  st4(base + i, y1);
-  st4(base + i + half, y2);
+  store8_f32(base + i, y1);
+  store8_f32(base + i + half, y2);
 }
 
 // Backward on the dq, dk column blocks of dqkv, in place: dz = r (dy - y mean(dy y)) with y
@@ -264,41 +240,41 @@ __global__ __launch_bounds__(256) void rope_qknorm_bwd_kernel(
     T* __restrict__ dqkv, const T* __restrict__ qkv, const T* __restrict__ cos_t,
     const T* __restrict__ sin_t, const float* __restrict__ rstd_qk, long long N, int Tn, int H,
     int hd, int qk_norm) {
-  const int D = H * hd, half = hd / 2, per_tok = D / 4;
+  const int D = H * hd, half = hd / 2, per_tok = D / 8;
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= N * per_tok) return;
   const long long tok = gid / per_tok;
-  const int p = (int)(gid % per_tok) * 4;
+  const int p = (int)(gid % per_tok) * 8;
   const int hq = p / half, i = p % half;
   const int t = (int)(tok % Tn);
   const long long off = tok * 3 * D + (hq < H ? 0 : D) + (hq % H) * hd;
-  float d1[4], d2[4], c[4], sn[4], o1[4], o2[4];
-  ld4(dqkv + off + i, d1);
-  ld4(dqkv + off + i + half, d2);
+  float d1[8], d2[8], c[8], sn[8], o1[8], o2[8];
+  load8_f32(dqkv + off + i, d1);
+  load8_f32(dqkv + off + i + half, d2);
   if (qk_norm) {
-    float y1[4], y2[4];
-    ld4(qkv + off + i, y1);
-    ld4(qkv + off + i + half, y2);
+    float y1[8], y2[8];
+    load8_f32(qkv + off + i, y1);
+    load8_f32(qkv + off + i + half, y2);
     const float r = rstd_qk[tok * 2 * H + hq];
     float dot = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dot += d1[e] * y1[e] + d2[e] * y2[e];
-    const float mean = group_sum(dot, half / 4) / (float)hd;
+    for (int e = 0; e < 8; ++e) dot += d1[e] * y1[e] + d2[e] * y2[e];
+    const float mean = group_sum(dot, half / 8) / (float)hd;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 8; ++e) {
       d1[e] = r * (d1[e] - y1[e] * mean);
       d2[e] = r * (d2[e] - y2[e] * mean);
     }
   }
-  ld4(cos_t + t * half + i, c);
-  ld4(sin_t + t * half + i, sn);
+  load8_f32(cos_t + t * half + i, c);
+  load8_f32(sin_t + t * half + i, sn);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
+  for (int e = 0; e < 8; ++e) {
     o1[e] = d1[e] * c[e] - d2[e] * sn[e];
     o2[e] = d1[e] * sn[e] + d2[e] * c[e];
   }
-  st4(dqkv + off + i, o1);
-  st4(dqkv + off + i + half, o2);
+  store8_f32(dqkv + off + i, o1);
+  store8_f32(dqkv + off + i + half, o2);
 }
 
 // ------------------------------------------------------------------ elementwise helpers
@@ -404,7 +380,7 @@ template <typename T>
 gpt_status launch_rope_qknorm_fwd(T* qkv, const T* cos_t, const T* sin_t, float* rstd_qk,
                                   long long N, int Tn, int H, int hd, int qk_norm, float eps,
                                   hipStream_t s) {
-  rope_qknorm_fwd_kernel<T><<<cdiv(N * H * hd / 4, 256), 256, 0, s>>>(qkv, cos_t, sin_t, rstd_qk,
+  rope_qknorm_fwd_kernel<T><<<cdiv(N * H * hd / 8, 256), 256, 0, s>>>(qkv, cos_t, sin_t, rstd_qk,
                                                                       N, Tn, H, hd, qk_norm, eps);
   return check_launch("rope+qknorm fwd");
 }
@@ -413,7 +389,7 @@ template <typename T>
 gpt_status launch_rope_qknorm_bwd(T* dqkv, const T* qkv, const T* cos_t, const T* sin_t,
                                   const float* rstd_qk, long long N, int Tn, int H, int hd,
                                   int qk_norm, hipStream_t s) {
-  rope_qknorm_bwd_kernel<T><<<cdiv(N * H * hd / 4, 256), 256, 0, s>>>(dqkv, qkv, cos_t, sin_t,
+  rope_qknorm_bwd_kernel<T><<<cdiv(N * H * hd / 8, 256), 256, 0, s>>>(dqkv, qkv, cos_t, sin_t,
                                                                       rstd_qk, N, Tn, H, hd, qk_norm);
   return check_launch("rope+qknorm bwd");
 }

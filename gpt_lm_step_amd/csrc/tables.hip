@@ -20,7 +20,6 @@ namespace gpt {
 
 namespace {
 
-constexpr int SCAN_THREADS = 256, SCAN_ITEMS = 8, SCAN_TILE = SCAN_THREADS * SCAN_ITEMS;
 constexpr int RS_THREADS = 256, RS_ROUNDS = 8, RS_TILE = RS_THREADS * RS_ROUNDS;
 constexpr int SEG_TILE = 64;  // sorted positions per wavefront in the segmented sums
 constexpr uint64_t HASH_MULT = 1000003ull;
