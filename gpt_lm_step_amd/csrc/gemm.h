@@ -18,7 +18,7 @@
 //    slice); both take 8 consecutive K values per lane, so operand fragments are identical;
 //  * the tile order keeps each XCD on a contiguous block of output tiles (L2 reuse), grouped
 //    along M so neighbouring tiles share operand panels;
-//  * epilogues are fused: bf16/fp32 stores, value addend, ReLU^2 (+ pre-activation),
+//  * epilogues are fused: bf16/fp32 stores, value addend, ReLU^2,
 //    dReLU^2, residual add, and beta-accumulation for weight gradients.
 // Header-only: every call site instantiates its own kernel symbol (a GemmSite tag), so
 // profiles name the projection a launch belongs to.
@@ -169,44 +169,42 @@ struct EpiQKV {
   GPT_EPI_CALL
 };
 
-// MLP up projection: hp = acc, act = relu(acc)^2.
+// MLP up projection: act = relu(acc)^2 (the only activation the backward needs: the derivative
+// 2 relu(h) equals 2 sqrt(act)).
 template <typename T>
 struct EpiRelu2 {
-  T* hp;
   T* act;
   long long ld;
   using Pre = NoPre;
   __device__ __forceinline__ Pre load(int, int) const { return {}; }
   __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre&) const {
-    const long long i = (long long)r * ld + c;
     float a[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float m = v[k] > 0.f ? v[k] : 0.f;
       a[k] = m * m;
     }
-    store4(hp + i, v);
-    store4(act + i, a);
+    store4(act + (long long)r * ld + c, a);
   }
   GPT_EPI_CALL
 };
 
-// Down-projection input gradient through ReLU^2: out = acc * 2 * relu(hp).
+// Down-projection input gradient through ReLU^2: out = acc * 2 relu(h) = acc * 2 sqrt(act).
 template <typename T>
 struct EpiDRelu2 {
-  const T* hp;
+  const T* act;
   T* out;
   long long ld;
   using Pre = Pre4<T>;
   __device__ __forceinline__ Pre load(int r, int c) const {
-    return pre_load(hp + (long long)r * ld + c);
+    return pre_load(act + (long long)r * ld + c);
   }
   __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre& a) const {
     float o[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float h = to_f32(a.x[k]);
-      o[k] = h > 0.f ? 2.f * h * v[k] : 0.f;
+      const float x = to_f32(a.x[k]);
+      o[k] = x > 0.f ? 2.f * __builtin_amdgcn_sqrtf(x) * v[k] : 0.f;
     }
     store4(out + (long long)r * ld + c, o);
   }

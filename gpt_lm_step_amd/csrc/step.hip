@@ -87,7 +87,7 @@ long long ce_chunk_rows(const gpt_config& c) {
 
 struct LayerBufs {
   float *x_in, *rstd_a, *rstd_qk, *lse, *x_mid, *rstd_b;
-  void *a, *qkv, *o, *b, *hp, *act;
+  void *a, *qkv, *o, *b, *act;
 };
 
 // Every device buffer of a step, carved from one workspace.  Element type sizes follow the
@@ -123,7 +123,6 @@ Plan carve_plan(const gpt_config& c, Carver& cv) {
     l.x_mid = cv.take<float>(N * D);
     l.rstd_b = cv.take<float>(N);
     l.b = T(N * D);
-    l.hp = T(N * F);
     l.act = T(N * F);
   }
   p.x_final = cv.take<float>(N * D);
@@ -261,8 +260,7 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
   // ---------------- forward
   for (int l = 0; l < Lc; ++l) {
     LayerBufs& b = p.L[l];
-    T *a = (T*)b.a, *qkv = (T*)b.qkv, *o = (T*)b.o, *bb = (T*)b.b, *hp = (T*)b.hp,
-      *act = (T*)b.act;
+    T *a = (T*)b.a, *qkv = (T*)b.qkv, *o = (T*)b.o, *bb = (T*)b.b, *act = (T*)b.act;
     float* x_out = l + 1 < Lc ? p.L[l + 1].x_in : p.x_final;
     STAGE("rmsnorm_fwd", 0, ND * (4 + es) + 4.0 * N,
           launch_rms_fwd<T>(b.x_in, a, b.rstd_a, N, D, eps, s));
@@ -279,7 +277,7 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
           launch_rms_fwd<T>(b.x_mid, bb, b.rstd_b, N, D, eps, s));
     STAGE("up_fwd", mm(N, F, D), 0,
           gemm<G_UP, T>(true, true, (int)N, F, D, bb, D, P + Ly.wfc[l], D,
-                        EpiRelu2<T>{hp, act, F}, s));
+                        EpiRelu2<T>{act, F}, s));
     STAGE("down_fwd", mm(N, D, F), 0,
           gemm<G_DOWN, T>(true, true, (int)N, D, F, act, F, P + Ly.wpr[l], F,
                           EpiResid{b.x_mid, x_out, D}, s));
@@ -316,11 +314,11 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
   for (int l = Lc - 1; l >= 0; --l) {
     LayerBufs& b = p.L[l];
     const T *a = (const T*)b.a, *qkv = (const T*)b.qkv, *o = (const T*)b.o, *bb = (const T*)b.b,
-            *hp = (const T*)b.hp, *act = (const T*)b.act;
+            *act = (const T*)b.act;
     // MLP: x_out = x_mid + relu(b Wfc^T)^2 Wpr^T
     STAGE("down_dgrad", mm(N, F, D), 0,
           gemm<G_DOWN_DGRAD, T>(true, false, (int)N, F, D, dx_t, D, P + Ly.wpr[l], F,
-                                EpiDRelu2<T>{hp, dact, F}, s));
+                                EpiDRelu2<T>{act, dact, F}, s));
     STAGE("down_wgrad", mm(D, F, N), 0,
           gemm_wgrad<G_DOWN_WGRAD, T>(false, false, D, F, (int)N, dx_t, D, act, F,
                                       EpiStoreF32{G + Ly.wpr[l], F, beta}, p.splitk,
