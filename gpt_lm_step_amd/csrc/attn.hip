@@ -139,31 +139,6 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // 2^x with the hardware instruction (v_exp_f32; results below 2^-126 flush to 0, 2^-inf = 0).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Buffer resource over [base, base + bytes): raw loads past the end read as zeros, so tiles that
-// run past the sequence need no branches.
-constexpr uint32_t OOB = 0x80000000u;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x8 __attribute__((ext_vector_type(8)));
-template <typename T>
-__device__ __forceinline__ vec8_t<T> bload8(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
-  if constexpr (sizeof(T) == 2) {
-    return __builtin_bit_cast(vec8_t<T>, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-  } else {
-    const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-    const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u, 0, 0);
-    u32x8 v;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[i] = lo[i];
-      v[4 + i] = hi[i];
-    }
-    return __builtin_bit_cast(vec8_t<T>, v);
-  }
-}
-
 // One R x HD tile of a token-major matrix (rows of `ld` elements) moved global -> registers ->
 // LDS as 8 x 8 blocks by the (R/8)*(HD/8) threads t in [0, NB).  A block can be written in row
 // layout lds[r][d] and/or transposed lds[d][r].  ROWFAST maps consecutive threads to consecutive

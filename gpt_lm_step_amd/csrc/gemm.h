@@ -264,30 +264,6 @@ struct Cfg {
   static constexpr int KV = BK / 8;                       // 8-element vectors per tile row
 };
 
-// Buffer resource over [base, base + bytes) (bytes <= 2^31): raw loads past the end read 0.
-constexpr uint32_t OOB = 0x80000000u;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-template <typename T>
-__device__ __forceinline__ vec8_t<T> bload8(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
-  if constexpr (sizeof(T) == 2) {
-    return __builtin_bit_cast(vec8_t<T>, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-  } else {
-    const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-    const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u, 0, 0);
-    typedef unsigned int u32x8 __attribute__((ext_vector_type(8)));
-    u32x8 v;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[i] = lo[i];
-      v[4 + i] = hi[i];
-    }
-    return __builtin_bit_cast(vec8_t<T>, v);
-  }
-}
-
 // Global -> registers -> LDS staging of one ROWS x BK operand tile.  KC tiles: thread v moves
 // 16 B vector v (row v / KV, chunk v % KV).  RC tiles: thread t moves the 8 x 8 block
 // (k-chunk t % (BK/8), row block t / (BK/8)): each global load instruction still reads whole

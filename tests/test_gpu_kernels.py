@@ -254,3 +254,34 @@ def test_softcap_cross_entropy(dtype, V):
     g = host(tz)
     assert rel_l2(g, g_want * 0.5 / nv) < (5e-3 if bf else 1e-5)
     assert np.all(g[2] == 0)
+
+
+@pytest.mark.parametrize("dtype,V,rows,cap", [(BF, 65536, 600, 15.0), (BF, 50304, 700, 15.0),
+                                              (BF, 2048, 2300, 15.0), (BF, 4096, 1500, 0.0),
+                                              (F32, 512, 3000, 15.0)])
+def test_cross_entropy_rows_per_workgroup(dtype, V, rows, cap):
+    """More rows than workgroups that fit the GPU at once, so each workgroup walks several rows
+    (loads of the next row in flight during the current one); rows of only negative logits,
+    saturated logits of both signs and ignored targets throughout."""
+    bf = dtype == BF
+    z0 = inputs.normal(21, (rows, V), 3.0, bf)
+    z0[1::7] = -np.abs(z0[1::7]) - 1.0                 # every logit negative
+    z0[2::11, 3] = 400.0                               # saturated above
+    z0[3::13, :] = -400.0                              # saturated below everywhere: uniform
+    if bf:
+        z0 = inputs.round_bf16(z0)                     # both sides see the same logits
+    tgt = np.random.default_rng(22).integers(0, V, rows).astype(np.int32)
+    tgt[::17] = -1
+    nv = int(np.sum(tgt >= 0))
+    tz = dev(z0, dtype)
+    loss = torch.empty(rows, device="cuda")
+    B.gptk_softcap_ce(tz, dev(tgt), torch.tensor([nv], dtype=torch.int32, device="cuda"), loss,
+                      cap=cap, grad_scale=1.0)
+    l_want, g_want = om.softcap_cross_entropy(z0.astype(np.float64), tgt.astype(np.int64), cap)
+    np.testing.assert_allclose(host(loss), l_want, rtol=(2e-5 if bf else 1e-5), atol=1e-5)
+    g = host(tz)
+    assert rel_l2(g, g_want / nv) < (5e-3 if bf else 1e-5)
+    # row by row too (a wrong row hides in the norm of 1000)
+    per_row = np.linalg.norm(g - g_want / nv, axis=1) / np.maximum(np.linalg.norm(g_want / nv, axis=1), 1e-30)
+    assert np.max(per_row[tgt >= 0]) < (2e-2 if bf else 1e-4)
+    assert np.all(g[tgt < 0] == 0)
