@@ -61,6 +61,7 @@ TRAFFIC_KERNELS = {
     "up_fwd": ("EpiRelu2", "gemm.h"),
     "down_fwd": ("EpiResidELi4E|EpiResid, 4>", "gemm.h"),
     "attn_bwd_dkdv": ("attn_bwd_dkdv_pipe_kernel", "attn.hip"),
+    "softcap_ce": ("9ce_kernelI|::ce_kernel<", "ce.hip"),
     "bigram_fwd (hash + gather-add, x0 table)": ("bigram_gather_kernel", "tables.hip"),
 }
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
