@@ -171,6 +171,38 @@ def test_gpt2_small_bf16_full_launch_sampled_sequences():
     _compare(cfg, res, step, loss, 1e-2, 3e-2, cos_min=0.999)
 
 
+def test_d32_bf16_full_launch_sampled_prefix():
+    """The d32 step at the size the bench times (B=8, T=2048, V=65536, 32 layers, device-drawn
+    N(0,0.02) bf16 weights, Zipf tokens) with targets only on the first P positions of one
+    sequence.  Attention is causal, so those positions never see later ones, and every later
+    query gets a zero output gradient (its dS is exactly zero): the loss and every gradient
+    equal the oracle's (fp64) on that P-token prefix alone."""
+    cfg = configs.D32
+    T, P, b0 = cfg.seq_len, 256, 5
+    flat = inputs.device_params(cfg, 103)
+    tok = inputs.step_tokens(cfg, 3)
+    tgt = np.full((cfg.batch, T), -1, np.int32)
+    tgt[b0, :P] = tok[b0, 1:P + 1]
+    ctx = B.gpt_init(cfg)
+    grads = torch.full((configs.param_elems(cfg),), float("nan"), device="cuda")
+    loss_t = torch.zeros(1, device="cuda")
+    B.gpt_fwd_bwd(ctx, dev(np.ascontiguousarray(tok[:, :T]).astype(np.int32)), dev(tgt), flat,
+                  grads, loss_t, 1.0, 0, None, None, None, None, None)
+    torch.cuda.synchronize()
+    loss = float(loss_t.item())
+    got = inputs.unflatten(cfg, host(grads))
+    del grads
+    params = inputs.unflatten(cfg, flat.float().cpu().numpy())
+    del flat, ctx
+    torch.cuda.empty_cache()
+    res = om.forward_backward(cfg.replace(batch=1, seq_len=P), params, tok[b0:b0 + 1, :P + 1])
+    assert abs(loss - res.loss) <= 1e-2 * abs(res.loss), (loss, res.loss)
+    for name, want in res.grads.items():
+        e = rel_l2(got[name], want)
+        assert e <= 3e-2, (name, e)
+        assert cosine(got[name], want) >= 0.999, name
+
+
 def test_speedrun_microbatch_with_tables_sampled():
     """Speedrun shape: GPT-2-small model + x0 bigram (2^21 rows), value bigram (2^20 rows) and
     the frozen trigram table (2^21 rows, N(0,1)) projected by wtri, one 8 x 1024 micro-batch;
