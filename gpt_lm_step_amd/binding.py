@@ -22,7 +22,8 @@ F32, BF16 = 0, 1
 EXPORTS = [
     "gpt_param_layout", "gpt_workspace_bytes", "gpt_init", "gpt_fwd_bwd", "gpt_check_errors",
     "gpt_profile", "gpt_profile_read", "gpt_destroy", "bigram_fwd", "bigram_workspace_bytes", "bigram_bwd_update",
-    "gpt_last_error", "gpt_status_string",
+    "gpt_last_error", "gpt_status_string", "gpt_opt_state_elems", "gpt_opt_workspace_bytes",
+    "gpt_opt_step", "gpt_lr_multiplier", "gpt_muon_momentum",
 ]
 # Every symbol include/gpt_kernels.h declares.
 KERNEL_EXPORTS = [
@@ -53,6 +54,14 @@ class gpt_profile_entry(C.Structure):
 class gpt_tensor_desc(C.Structure):
     _fields_ = [("name", C.c_char * 48), ("offset_elems", C.c_int64), ("ndim", C.c_int32),
                 ("shape", C.c_int64 * 2)]
+
+
+class gpt_opt_hparams(C.Structure):
+    _fields_ = [("lr_matrix", C.c_float), ("lr_embedding", C.c_float),
+                ("lr_unembedding", C.c_float), ("lr_mult", C.c_float), ("momentum", C.c_float),
+                ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
+                ("weight_decay", C.c_float), ("grad_clip", C.c_float), ("nesterov", C.c_int32),
+                ("ns_steps", C.c_int32), ("adam_step", C.c_int64)]
 
 
 def lib() -> C.CDLL:
@@ -91,6 +100,12 @@ def lib() -> C.CDLL:
             "gptk_attention_fwd": (i32, [i32, vp, vp, vp, i32, i32, i32, i32, vp]),
             "gptk_attention_bwd": (i32, [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]),
             "gptk_softcap_ce": (i32, [i32, vp, i64, vp, i64, i32, f32, f32, vp, vp, vp]),
+            "gpt_opt_state_elems": (i64, [cfgp]),
+            "gpt_opt_workspace_bytes": (i32, [cfgp, C.POINTER(sz)]),
+            "gpt_opt_step": (i32, [cfgp, vp, vp, vp, vp, C.POINTER(gpt_opt_hparams), vp, sz, vp,
+                                   vp]),
+            "gpt_lr_multiplier": (C.c_double, [i64, i64, C.c_double, C.c_double, C.c_double]),
+            "gpt_muon_momentum": (C.c_double, [i64]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -303,3 +318,39 @@ def gptk_softcap_ce(z, targets, n_valid, loss_rows, cap: float = 15.0, grad_scal
     _check(lib().gptk_softcap_ce(_dtype_code(z), _ptr(z), z.stride(0), _ptr(targets), rows, V,
                                  cap, grad_scale, _ptr(n_valid), _ptr(loss_rows),
                                  _stream(stream)))
+
+
+# ---------------------------------------------------------------- dense optimizer step
+def gpt_opt_state_elems(cfg: GPTConfig) -> int:
+    c = make_config(cfg)
+    n = int(lib().gpt_opt_state_elems(C.byref(c)))
+    if n < 0:
+        raise GptError(GPT_EINVAL, lib().gpt_last_error().decode())
+    return n
+
+
+def gpt_opt_workspace_bytes(cfg: GPTConfig) -> int:
+    c = make_config(cfg)
+    b = C.c_size_t(0)
+    _check(lib().gpt_opt_workspace_bytes(C.byref(c), C.byref(b)))
+    return b.value
+
+
+def gpt_opt_step(cfg: GPTConfig, master, params, grads, state, hp: dict, workspace,
+                 grad_norm=None, stream=None):
+    """One dense optimizer step (see gpt.h).  hp: the gpt_opt_hparams fields by name."""
+    c = make_config(cfg)
+    h = gpt_opt_hparams(**hp)
+    _check(lib().gpt_opt_step(C.byref(c), _ptr(master), _ptr(params), _ptr(grads), _ptr(state),
+                              C.byref(h), _ptr(workspace), workspace.numel(), _ptr(grad_norm),
+                              _stream(stream)))
+
+
+def gpt_lr_multiplier(it: int, num_iterations: int, warmup_ratio: float, warmdown_ratio: float,
+                      final_lr_frac: float) -> float:
+    return float(lib().gpt_lr_multiplier(it, num_iterations, warmup_ratio, warmdown_ratio,
+                                         final_lr_frac))
+
+
+def gpt_muon_momentum(it: int) -> float:
+    return float(lib().gpt_muon_momentum(it))

@@ -24,6 +24,9 @@
 // profiles name the projection a launch belongs to.
 #pragma once
 
+#include <type_traits>
+#include <utility>
+
 #include "kernels.h"
 
 namespace gpt {
@@ -133,6 +136,41 @@ struct EpiSplit {
 };
 
 // out = res + acc (fp32 residual stream; out may equal res).
+// Batched bf16 products of the Newton-Schulz iteration (matrix z of a batch at out + z * bs):
+// a plain store, and out = alpha * acc + beta * add with `add` in the output's layout.
+struct EpiNsStore {
+  bf16* out;
+  long long ld, bs;
+  using Pre = NoPre;
+  __device__ __forceinline__ void at_batch(int z) { out += (long long)z * bs; }
+  __device__ __forceinline__ Pre load(int, int) const { return {}; }
+  __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre&) const {
+    store4(out + (long long)r * ld + c, v);
+  }
+  GPT_EPI_CALL
+};
+struct EpiNsCombine {
+  bf16* out;
+  const bf16* add;
+  long long ld, bs;
+  float alpha, beta;
+  using Pre = Pre4<bf16>;
+  __device__ __forceinline__ void at_batch(int z) {
+    out += (long long)z * bs;
+    add += (long long)z * bs;
+  }
+  __device__ __forceinline__ Pre load(int r, int c) const {
+    return pre_load(add + (long long)r * ld + c);
+  }
+  __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre& a) const {
+    float o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = alpha * v[i] + beta * to_f32(a.x[i]);
+    store4(out + (long long)r * ld + c, o);
+  }
+  GPT_EPI_CALL
+};
+
 struct EpiResid {
   const float* res;
   float* out;
@@ -237,7 +275,7 @@ struct EpiAddRows {
 enum GemmSite {
   G_TEST = 0, G_QKV, G_OUT, G_UP, G_DOWN, G_HEAD, G_HEAD_DGRAD, G_HEAD_WGRAD, G_DOWN_DGRAD,
   G_DOWN_WGRAD, G_UP_DGRAD, G_UP_WGRAD, G_OUT_DGRAD, G_OUT_WGRAD, G_QKV_DGRAD, G_QKV_WGRAD,
-  G_TRI, G_TRI_WGRAD
+  G_TRI, G_TRI_WGRAD, G_NS_GRAM, G_NS_POLY, G_NS_APPLY
 };
 
 namespace gemm_detail {
@@ -458,6 +496,12 @@ __global__ __launch_bounds__(THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_
   }
 }
 
+// Epilogues with an at_batch(z) member serve batched launches.
+template <class E, class = void>
+struct has_batch : std::false_type {};
+template <class E>
+struct has_batch<E, std::void_t<decltype(std::declval<E&>().at_batch(0))>> : std::true_type {};
+
 // ---------------------------------------------------------------- bf16: DMA-staged kernel
 // Operand tiles travel global -> LDS by buffer loads that write LDS directly (16 B per lane,
 // 1 KB per wave instruction, lane l to byte 16*l of the instruction's LDS block), in the
@@ -567,8 +611,14 @@ template <int BM, int BN, int WGM, int WGN, int BK, int NS, bool A_KC, bool B_KC
           int SITE>
 __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_dma_kernel(
     const bf16* A, long long lda, const bf16* B, long long ldb, int M,
-    int N, int K, uint32_t a_bytes, uint32_t b_bytes, Epi epi, int kps) {
+    int N, int K, uint32_t a_bytes, uint32_t b_bytes, Epi epi, int kps, long long a_bs,
+    long long b_bs) {
   constexpr int NW = WGM * WGN, WTM = BM / WGM, WTN = BN / WGN;
+  // batch z = blockIdx.z: operands at A + z * a_bs, B + z * b_bs; epilogues that hold batched
+  // outputs move their pointers themselves
+  A += (long long)blockIdx.z * a_bs;
+  B += (long long)blockIdx.z * b_bs;
+  if constexpr (has_batch<Epi>::value) epi.at_batch(blockIdx.z);
   // split-K: workgroups with blockIdx.y = s take K range [s * kps, min(K, (s + 1) * kps))
   {
     const int k0 = blockIdx.y * kps;
@@ -787,9 +837,10 @@ inline long long operand_bytes(bool kc, long long rows, long long K, long long l
 
 template <int BM, int BN, int WGM, int WGN, class Epi, int SITE>
 void launch_dma(bool a_kc, bool b_kc, int M, int N, int K, const bf16* A, long long lda,
-                const bf16* B, long long ldb, const Epi& epi, hipStream_t s, int splits = 1) {
+                const bf16* B, long long ldb, const Epi& epi, hipStream_t s, int splits = 1,
+                int batch = 1, long long a_bs = 0, long long b_bs = 0) {
   const int kps = splits > 1 ? (int)cdiv(cdiv(K, splits), 64) * 64 : K;  // K per split
-  dim3 grid((unsigned)(cdiv(M, BM) * cdiv(N, BN)), (unsigned)cdiv(K, kps));
+  dim3 grid((unsigned)(cdiv(M, BM) * cdiv(N, BN)), (unsigned)cdiv(K, kps), (unsigned)batch);
   // each split's operand spans at most these bytes from its own start
   const uint32_t ab = (uint32_t)operand_bytes(a_kc, M, kps, lda, 2);
   const uint32_t bb = (uint32_t)operand_bytes(b_kc, N, kps, ldb, 2);
@@ -798,7 +849,7 @@ void launch_dma(bool a_kc, bool b_kc, int M, int N, int K, const bf16* A, long l
   // (the 64-wide two-stage form of that layout does not fit the registers)
 #define GEMM_DMA(AK, BK_, KT, NS_)                                                               \
   gemm_dma_kernel<BM, BN, WGM, WGN, KT, NS_, AK, BK_, Epi, SITE><<<grid, 64 * WGM * WGN, 0, s>>>( \
-      A, lda, B, ldb, M, N, K, ab, bb, epi, kps)
+      A, lda, B, ldb, M, N, K, ab, bb, epi, kps, a_bs, b_bs)
   if (a_kc && b_kc) GEMM_DMA(true, true, 64, 2);
   else if (a_kc) GEMM_DMA(true, false, 64, 2);
   else if (b_kc) GEMM_DMA(false, true, 32, 4);
@@ -858,6 +909,37 @@ inline gpt_status gemm(bool a_kc, bool b_kc, int M, int N, int K, const T* A, lo
     }
   });
   return check_launch("gemm");
+}
+
+// Batched bf16 GEMM: C_z = A_z B_z^T for z < batch, with A_z = A + z * a_bs and B_z = B + z * b_bs
+// (elements) in the layouts of gemm(), and an epilogue whose at_batch(z) moves its outputs.  The
+// tile size follows the total tile count over the batch.
+template <int SITE, class Epi>
+inline gpt_status gemm_batched(bool a_kc, bool b_kc, int M, int N, int K, const bf16* A,
+                               long long lda, long long a_bs, const bf16* B, long long ldb,
+                               long long b_bs, int batch, const Epi& epi, hipStream_t s) {
+  static_assert(gemm_detail::has_batch<Epi>::value, "batched launches need an at_batch epilogue");
+  if (batch <= 0 || M <= 0 || N <= 0) return GPT_OK;
+  if (batch > 65535) return fail(GPT_ESHAPE, "gemm_batched: at most 65535 matrices");
+  if (K <= 0 || K % 8) return fail(GPT_ESHAPE, "gemm: K must be a positive multiple of 8");
+  if (lda % 8 || ldb % 8 || a_bs % 8 || b_bs % 8)
+    return fail(GPT_ESHAPE, "gemm_batched: leading dimensions and batch strides must be multiples of 8");
+  if ((!a_kc && M % 8) || (!b_kc && N % 8))
+    return fail(GPT_ESHAPE, "gemm: row-contiguous operands need a multiple of 8 rows");
+  if (N % 4) return fail(GPT_ESHAPE, "gemm: N must be a multiple of 4");
+  if (((uintptr_t)A | (uintptr_t)B) % 16) return fail(GPT_EINVAL, "gemm: operands must be 16-byte aligned");
+  if (gemm_detail::operand_bytes(a_kc, M, K, lda, 2) > (1LL << 31) ||
+      gemm_detail::operand_bytes(b_kc, N, K, ldb, 2) > (1LL << 31))
+    return fail(GPT_ESHAPE, "gemm: each operand must span at most 2 GiB");
+  if ((long long)cdiv(M, 128) * cdiv(N, 128) >= (1LL << 31)) return fail(GPT_ESHAPE, "gemm: too many tiles");
+  const long long big_tiles = (long long)cdiv(M, 256) * cdiv(N, 256) * batch;
+  if (big_tiles >= 240)
+    gemm_detail::launch_dma<256, 256, 2, 4, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s,
+                                                       1, batch, a_bs, b_bs);
+  else
+    gemm_detail::launch_dma<128, 128, 2, 2, Epi, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, epi, s,
+                                                       1, batch, a_bs, b_bs);
+  return check_launch("gemm_batched");
 }
 
 namespace gemm_detail {

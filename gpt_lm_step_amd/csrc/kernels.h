@@ -1,9 +1,31 @@
 // Host-side launchers of the gfx950 kernels (internal to libgpt; not part of the ABI).
 #pragma once
 
+#include <string>
+#include <vector>
+
 #include "common.h"
 
 namespace gpt {
+
+// ---------------------------------------------------------------- parameter layout (step.hip)
+// Offsets (elements) of every tensor of the flat parameter / gradient buffer, in the order of
+// gpt_param_layout, each a multiple of PARAM_ALIGN.
+constexpr int PARAM_ALIGN = 64;
+inline long long align_elems(long long n) { return (n + PARAM_ALIGN - 1) / PARAM_ALIGN * PARAM_ALIGN; }
+struct Layout {
+  struct Entry {
+    std::string name;
+    long long off, rows, cols;
+  };
+  std::vector<Entry> e;
+  long long total = 0;
+  long long wte, lm_head, wtri = -1;
+  std::vector<long long> wqkv, wo, wfc, wpr;
+};
+Layout make_layout(const gpt_config& c);
+// Argument checks shared by every entry point that takes a configuration.
+gpt_status validate(const gpt_config* c);
 
 // ---------------------------------------------------------------- tables / segments
 // Hash + gather-add of one n-gram table (bigram_fwd).

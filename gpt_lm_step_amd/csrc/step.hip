@@ -11,22 +11,6 @@
 #include "gemm.h"
 
 namespace gpt {
-namespace {
-
-constexpr int PARAM_ALIGN = 64;
-
-long long align_elems(long long n) { return (n + PARAM_ALIGN - 1) / PARAM_ALIGN * PARAM_ALIGN; }
-
-struct Layout {
-  struct Entry {
-    std::string name;
-    long long off, rows, cols;
-  };
-  std::vector<Entry> e;
-  long long total = 0;
-  long long wte, lm_head, wtri = -1;
-  std::vector<long long> wqkv, wo, wfc, wpr;
-};
 
 Layout make_layout(const gpt_config& c) {
   Layout L;
@@ -73,6 +57,8 @@ gpt_status validate(const gpt_config* c) {
     return fail(GPT_ERANGE, "rms_eps, rope_base or softcap out of range");
   return GPT_OK;
 }
+
+namespace {
 
 
 // Tokens of one head/cross-entropy chunk: all tokens when the bf16/fp32 logits fit in 2 GiB

@@ -141,6 +141,64 @@ gpt_status gpt_profile_read(gpt_ctx* ctx, gpt_profile_entry* out, int32_t* count
 
 gpt_status gpt_destroy(gpt_ctx* ctx);
 
+/* ---- Dense optimizer step (the training script of the "$1000 tier nanochat run" discussion:
+ * gradient clipping in its accumulation loop, setup_optimizers, the Muon class with
+ * zeropower_via_newtonschulz5, get_lr_multiplier, get_muon_momentum; the modded-nanogpt README
+ * for the bfloat16 Newton-Schulz iteration).  One call, after gpt_fwd_bwd has left the full
+ * gradient in `grads`:
+ *   1. norm = global L2 norm of grads; every gradient is scaled by f = min(1, grad_clip /
+ *      (norm + 1e-6)) (f = 1 when grad_clip == 0).
+ *   2. Adam (bias-corrected, decoupled weight decay) on wte with lr = lr_embedding * s * lr_mult
+ *      and on lm_head with lr = lr_unembedding * s * lr_mult, s = (d_model / 768)^-1/2:
+ *      m += (1-beta1)(g-m); v = beta2 v + (1-beta2) g^2;
+ *      w = w (1 - lr wd) - lr / (1-beta1^t) * m / (sqrt(v) / sqrt(1-beta2^t) + eps).
+ *   3. Muon on every block matrix (q, k, v - the three D-row blocks of wqkv, each on its own -,
+ *      wo, wfc, wpr, and wtri when present): buf += (1-momentum)(g-buf);
+ *      u = g + momentum (buf - g) (nesterov) or buf; X = NS(u); w -= lr_matrix * lr_mult *
+ *      sqrt(max(1, rows/cols)) X, where NS is ns_steps quintic Newton-Schulz steps in bf16 on
+ *      u / (||bf16(u)||_F + 1e-7): A = X X^T, B = -4.7750 A + 2.0315 A A, X = 3.4445 X + B X
+ *      (tall matrices transposed), each new matrix rounded once to bf16 from fp32 accumulation.
+ *   master  fp32 weights, flat layout (gpt_param_layout), updated in place.
+ *   params  bf16 configurations: the bf16 copy that gpt_fwd_bwd reads, rewritten from the new
+ *           master (round to nearest even); may be NULL.  fp32 configurations: NULL or master.
+ *   grads   fp32 gradients, flat layout (read only; the clip factor is applied on the fly).
+ *   state   fp32 [gpt_opt_state_elems]: Muon momentum of every block matrix and Adam's first
+ *           moment of wte and lm_head at their flat-layout offsets, then Adam's second moments of
+ *           wte and lm_head (each padded to 64 elements).  Zero it before the first step.
+ *   workspace  at least gpt_opt_workspace_bytes, 256-byte aligned (Newton-Schulz buffers of one
+ *           shape group, partial sums); grad_norm: fp32 device scalar (may be NULL) receiving
+ *           the norm before clipping.
+ * Deterministic: every reduction has a fixed order.  Stream-ordered; never synchronises. */
+typedef struct {
+  float lr_matrix;       /* Muon learning rate (0.02) */
+  float lr_embedding;    /* Adam lr of wte before the d_model scaling (0.2) */
+  float lr_unembedding;  /* Adam lr of lm_head before the d_model scaling (0.004) */
+  float lr_mult;         /* schedule factor of this step, e.g. gpt_lr_multiplier */
+  float momentum;        /* Muon momentum of this step, e.g. gpt_muon_momentum */
+  float beta1, beta2;    /* Adam (0.8, 0.95) */
+  float eps;             /* Adam (1e-10) */
+  float weight_decay;    /* Adam (0) */
+  float grad_clip;       /* maximum global gradient norm (1.0); 0 disables clipping */
+  int32_t nesterov;      /* 1: Nesterov form of the momentum */
+  int32_t ns_steps;      /* Newton-Schulz steps (5) */
+  int64_t adam_step;     /* Adam steps taken including this one (1 on the first) */
+} gpt_opt_hparams;
+
+/* fp32 elements of optimizer state for cfg [host]; -1 for an invalid configuration. */
+int64_t gpt_opt_state_elems(const gpt_config* cfg);
+/* Device workspace in bytes for gpt_opt_step [host]. */
+gpt_status gpt_opt_workspace_bytes(const gpt_config* cfg, size_t* bytes);
+gpt_status gpt_opt_step(const gpt_config* cfg, float* master, void* params, const float* grads,
+                        float* state, const gpt_opt_hparams* hp, void* workspace,
+                        size_t ws_bytes, float* grad_norm, hipStream_t stream);
+/* Schedules of the same script [host, pure]: the lr factor of iteration `it` (linear warmup over
+ * round(warmup_ratio * num_iterations) iterations, then 1, then linear warmdown over the last
+ * round(warmdown_ratio * num_iterations) to final_lr_frac), and Muon's momentum (0.85 rising
+ * linearly to 0.95 over 300 iterations).  round() is to nearest, ties to even. */
+double gpt_lr_multiplier(int64_t it, int64_t num_iterations, double warmup_ratio,
+                         double warmdown_ratio, double final_lr_frac);
+double gpt_muon_momentum(int64_t it);
+
 /* Hashed n-gram gather-add (decoder-rtx bigram/trigram tables).  For each sequence b and
  * position t with current id c = tokens[b,t], previous ids p = tokens[b,t-1], pp = tokens[b,t-2]
  * (a missing previous id is `vocab`):

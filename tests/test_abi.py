@@ -120,3 +120,45 @@ def test_wgrad_split_k_workspace(M, N, K, splits):
     """Split-K weight-gradient plan: one fp32 M x N partial per split, none when not split."""
     assert B.gptk_gemm_wgrad_ws_floats(M, N, K) == (splits * M * N if splits > 1 else 0)
     assert B.gptk_gemm_wgrad_ws_floats(0, N, K) == 0
+
+
+def test_optimizer_schedules_match_hand_worked_values():
+    """The library's host schedules against the same hand-worked values as the oracle's."""
+    path = os.path.join(ROOT, "tests", "golden", "optim_schedules.txt")
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        f = line.split()
+        if f[0] == "lr":
+            got = B.gpt_lr_multiplier(int(f[1]), int(f[2]), float(f[3]), float(f[4]), float(f[5]))
+        else:
+            got = B.gpt_muon_momentum(int(f[1]))
+        assert got == pytest.approx(float(f[-1]), abs=1e-12), line
+
+
+@pytest.mark.parametrize("cfg", list(configs.PRESETS.values()), ids=list(configs.PRESETS))
+def test_optimizer_state_and_workspace_sizes(cfg):
+    total = configs.param_elems(cfg)
+    vd = cfg.vocab * cfg.d_model
+    assert B.gpt_opt_state_elems(cfg) == total + 2 * ((vd + 63) // 64 * 64)
+    ws = B.gpt_opt_workspace_bytes(cfg)
+    D, F, L = cfg.d_model, cfg.d_mlp, cfg.n_layer
+    # the q/k/v/o group: X, X' (4L matrices of D x D) and A, B (D x D each) in bf16
+    assert ws >= 4 * (4 * L * D * D * 2)
+    assert ws >= 2 * (L * F * D * 2)
+
+
+def test_optimizer_step_argument_checks_without_gpu():
+    cfg = configs.TINY
+    c = B.make_config(cfg)
+    L = B.lib()
+    hp = B.gpt_opt_hparams(0.02, 0.2, 0.004, 1.0, 0.95, 0.8, 0.95, 1e-10, 0.0, 1.0, 1, 5, 1)
+    need = B.gpt_opt_workspace_bytes(cfg)
+    args = lambda ws, n, h=hp: L.gpt_opt_step(C.byref(c), 256, None, 256, 256, C.byref(h), ws, n, None, None)
+    assert args(None, need) == B.GPT_EINVAL                       # no workspace
+    assert args(256, need - 1) == B.GPT_EWORKSPACE               # too small
+    bad = B.gpt_opt_hparams(0.02, 0.2, 0.004, 1.0, 0.95, 0.8, 1.5, 1e-10, 0.0, 1.0, 1, 5, 1)
+    assert args(256, need, bad) == B.GPT_ERANGE                   # beta2 >= 1
+    zero_step = B.gpt_opt_hparams(0.02, 0.2, 0.004, 1.0, 0.95, 0.8, 0.95, 1e-10, 0.0, 1.0, 1, 5, 0)
+    assert args(256, need, zero_step) == B.GPT_ERANGE             # Adam step count starts at 1
+    assert L.gpt_opt_step(C.byref(c), None, None, 256, 256, C.byref(hp), 256, need, None, None) == B.GPT_EINVAL
