@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of one decoder training step (forward + hand-written backward) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload d32|gpt2|tiny|tables|speedrun]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload d32|gpt2|tiny|tables|speedrun|opt]
 
 Prints ONE JSON line.  Dense workloads (d32 default, gpt2, tiny): tokens/s of the whole fwd+bwd
 step (inputs already in HBM), MFU against the bf16 dense MFMA peak using the nanochat
@@ -30,7 +30,7 @@ PEAK_FP32 = 157.3e12     # MI355X fp32 (matrix and vector), FLOP/s
 PEAK_HBM = 8.0e12        # MI355X HBM3E, B/s
 METRIC = "train tokens/sec (fwd+bwd) on 1 MI355X + MFU vs bf16 MFMA peak"
 DENSE = {"d32": configs.D32, "gpt2": configs.GPT2_SMALL, "tiny": configs.TINY}
-WORKLOADS = sorted(list(DENSE) + ["tables", "speedrun", "copy"])
+WORKLOADS = sorted(list(DENSE) + ["tables", "speedrun", "copy", "opt"])
 # Stages made of several kernels (their time is not one kernel's launch duration); the weight-
 # gradient stages join them when their shape is split over K (see split_stages).
 MULTI_KERNEL = {"wte_segsum"}
@@ -501,6 +501,113 @@ def bench_speedrun(a, B):
     return out
 
 
+def ns_groups(cfg):
+    """(count, rows, cols) of every batch of Muon matrices (q/k/v/o blocks, MLP up, MLP down,
+    trigram projection)."""
+    D, F, L = cfg.d_model, cfg.d_mlp, cfg.n_layer
+    g = [(4 * L, D, D), (L, F, D), (L, D, F)]
+    if cfg.has_trigram:
+        g.append((1, D, D))
+    return g
+
+
+def ns_work(cfg, steps=5):
+    """Newton-Schulz GEMM flops of one optimizer step and its launches (3 per step and batch):
+    X X^T (2 S^2 L), c A A + b A (2 S^3), B X + a X (2 R C S), S = min(R, C), L = max(R, C)."""
+    flops, launches = 0.0, 0
+    for count, R, C in ns_groups(cfg):
+        S, L = min(R, C), max(R, C)
+        flops += count * steps * (2.0 * S * S * L + 2.0 * S ** 3 + 2.0 * R * C * S)
+        launches += 3 * steps
+    return flops, launches
+
+
+def opt_bytes(cfg):
+    """Algorithmic bytes of the optimizer's memory-bound kernels per step: the norm pass reads
+    the gradients; the update reads them again with the fp32 weights and first moments (written
+    back) and writes the bf16 copy; Adam also reads and writes its second moments; Muon writes
+    its bf16 input, which the scaling reads and writes and the final update reads."""
+    n = configs.param_elems(cfg)
+    vd = cfg.vocab * cfg.d_model
+    nm = sum(c * r * k for c, r, k in ns_groups(cfg))
+    return 4 * n + (4 + 8 + 8 + 2) * n + 8 * 2 * vd + (2 + 4 + 2) * nm
+
+
+def bench_opt(a, B):
+    import torch
+    cfg = configs.D32
+    n = configs.param_elems(cfg)
+    g = torch.Generator(device="cuda").manual_seed(inputs.seeds_for(cfg.name)["weights"])
+    master = torch.randn(n, device="cuda", generator=g) * 0.02
+    params = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    grads = torch.randn(n, device="cuda", generator=g) * 0.05
+    state = torch.zeros(B.gpt_opt_state_elems(cfg), device="cuda")
+    ws = torch.empty(B.gpt_opt_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    gnorm = torch.zeros(1, device="cuda")
+    count = [0]
+
+    def hp(ns_steps):
+        count[0] += 1
+        return dict(lr_matrix=0.02, lr_embedding=0.2, lr_unembedding=0.004,
+                    lr_mult=B.gpt_lr_multiplier(0, 1000, 0.0, 0.2, 0.0),
+                    momentum=B.gpt_muon_momentum(0), beta1=0.8, beta2=0.95, eps=1e-10,
+                    weight_decay=0.0, grad_clip=1.0, nesterov=1, ns_steps=ns_steps,
+                    adam_step=count[0])
+
+    ms, wall = time_steps(lambda: B.gpt_opt_step(cfg, master, params, grads, state, hp(5), ws, gnorm),
+                          a.steps, a.warmup)
+    ms0, _ = time_steps(lambda: B.gpt_opt_step(cfg, master, params, grads, state, hp(0), ws, gnorm),
+                        a.steps, a.warmup)
+    assert np.isfinite(float(gnorm.item()))
+    flops, launches = ns_work(cfg)
+    ns_ms = max(ms - ms0, 1e-6)
+    ach = flops / (ns_ms / 1e3)
+    roof = {"bound": "mfma", "kernel": "Newton-Schulz batched GEMMs (gemm_dma_kernel, NS sites)",
+            "achieved": round(ach / 1e12, 1), "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_BF16, 4), "avg_launch_ms": round(ns_ms / launches, 4),
+            "algorithmic_per_launch": flops / launches, "traffic": None,
+            "launches_per_step": launches,
+            "timing": "HIP events: the step with 5 Newton-Schulz steps minus the step with none"}
+    nbytes = opt_bytes(cfg)
+    parts = {"newton_schulz": {"ms_per_step": round(ns_ms, 3), "launches": launches,
+                               "achieved": round(ach / 1e12, 1), "unit": "TFLOP/s",
+                               "frac": round(ach / PEAK_BF16, 4)},
+             "elementwise (clip, Adam, momentum, scaling, update)": {
+                 "ms_per_step": round(ms0, 3), "achieved": round(nbytes / (ms0 / 1e3) / 1e9, 1),
+                 "unit": "GB/s", "frac": round(nbytes / (ms0 / 1e3) / PEAK_HBM, 4)}}
+    out = {"metric": "dense optimizer step time (clip + Adam + Muon with 5 bf16 Newton-Schulz steps)",
+           "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+           "ms_per_step": round(ms, 3), "higher_is_better": False, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (N(0,0.02) weights, N(0,0.05) gradients)",
+           "config": {"workload": f"{cfg.name} optimizer step", "params": n,
+                      "muon_matrices": sum(c for c, _, _ in ns_groups(cfg))},
+           "wall_s": round(wall, 3), "roofline": roof, "parts": parts}
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_opt(cfg)
+    return out
+
+
+def cpu_baseline_opt(cfg):
+    """The oracle's Muon update (fp64 numpy, bf16 Newton-Schulz) of one D x D matrix, scaled to
+    the whole step by Newton-Schulz flops."""
+    from threadpoolctl import threadpool_limits
+    from oracle import optim as oo
+    cores = _cores()
+    rng = np.random.default_rng(5)
+    D = cfg.d_model
+    p = rng.standard_normal((D, D)) * 0.02
+    g = rng.standard_normal((D, D)) * 0.05
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        oo.muon_update(p, g, np.zeros_like(g), 0.02, 0.85, True, 5, bf16=True)
+        dt = time.perf_counter() - t0
+    flops, _ = ns_work(cfg)
+    one = 5 * (2.0 * D ** 3 * 3)
+    return {"value": round(dt * flops / one * 1e3, 1), "unit": "ms", "cores": cores, "kind": "oracle",
+            "sample": f"one {D} x {D} Muon update with 5 bf16 Newton-Schulz steps (fp64 numpy), "
+                      f"{dt:.1f} s, scaled to the step's Newton-Schulz flops"}
+
+
 def main():
     a = parse()
     if a.record_traffic:
@@ -524,6 +631,8 @@ def main():
         out = bench_tables(a, B)
     elif a.workload == "speedrun":
         out = bench_speedrun(a, B)
+    elif a.workload == "opt":
+        out = bench_opt(a, B)
     else:
         out = bench_dense(a, B)
     print(json.dumps(out), flush=True)
