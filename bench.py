@@ -11,7 +11,9 @@ instrumented pass), and the CPU oracle timed on a bounded sample of the same wor
 host's cores.  `tables`: the hashed-bigram gather and the fused scatter-reduce + per-row update
 of both tables over 196,608 tokens.  `speedrun`: one optimizer step of the GPT-2-small model
 with both bigram tables and the trigram table, 24 accumulated micro-batches of 8 x 1024 tokens,
-then one in-place update per table.
+then one in-place update per table.  `opt`: the dense optimizer step of the d32 model.
+`decode`: batched generation with the key/value cache on the d32 model (batch 8, 1024-token
+prompt, then one token per sequence per step: cached forward + top-k sampling).
 """
 from __future__ import annotations
 
@@ -30,7 +32,7 @@ PEAK_FP32 = 157.3e12     # MI355X fp32 (matrix and vector), FLOP/s
 PEAK_HBM = 8.0e12        # MI355X HBM3E, B/s
 METRIC = "train tokens/sec (fwd+bwd) on 1 MI355X + MFU vs bf16 MFMA peak"
 DENSE = {"d32": configs.D32, "gpt2": configs.GPT2_SMALL, "tiny": configs.TINY}
-WORKLOADS = sorted(list(DENSE) + ["tables", "speedrun", "copy", "opt"])
+WORKLOADS = sorted(list(DENSE) + ["tables", "speedrun", "copy", "opt", "decode"])
 # Stages made of several kernels (their time is not one kernel's launch duration); the weight-
 # gradient stages join them when their shape is split over K (see split_stages).
 MULTI_KERNEL = {"wte_segsum"}
@@ -608,6 +610,91 @@ def cpu_baseline_opt(cfg):
                       f"{dt:.1f} s, scaled to the step's Newton-Schulz flops"}
 
 
+def decode_bytes(cfg, batch, p_first, steps):
+    """Algorithmic HBM bytes per decode step, averaged over `steps` steps whose new tokens sit at
+    positions p_first, p_first + 1, ...: every weight matrix and the LM head read once (bf16), one
+    embedding row per sequence, the cached keys and values of every attended position read and
+    the new ones written, the fp32 logits written and read back by the sampler."""
+    D, F, L, V = cfg.d_model, cfg.d_mlp, cfg.n_layer, cfg.vocab
+    kv_row = 2 * D * 2                              # one position's key + value, one layer, bf16
+    weights = L * (4 * D * D + 2 * D * F) * 2 + V * D * 2
+    total = 0.0
+    for s in range(steps):
+        attended = p_first + s + 1
+        total += (weights + batch * D * 2 + L * batch * kv_row * (attended + 1)
+                  + batch * V * 4 * 2)
+    return total / steps
+
+
+def bench_decode(a, B):
+    import torch
+    cfg = configs.D32
+    batch, prompt, top_k, temperature = 8, 1024, 50, 1.0
+    seeds = inputs.seeds_for(cfg.name)
+    flat = inputs.device_params(cfg, seeds["weights"])
+    max_seq = prompt + a.warmup + a.steps
+    ctx = B.gpt_infer_init(cfg, batch, max_seq)
+    g = torch.Generator(device="cuda").manual_seed(seeds["tokens"])
+    u = torch.rand(a.warmup + a.steps + 1, batch, device="cuda", generator=g)
+    tok = torch.from_numpy(inputs.zipf_tokens(seeds["tokens"], (batch, prompt), cfg.vocab)).cuda()
+    logits = torch.empty(batch, cfg.vocab, device="cuda")
+    nxt = torch.empty(batch, 1, dtype=torch.int32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    B.gpt_infer_forward(ctx, flat, tok, logits)
+    e1.record()
+    B.gpt_sample(logits, temperature, top_k, u[0], nxt.view(-1))
+    torch.cuda.synchronize()
+    prefill_ms = e0.elapsed_time(e1)
+    i = [1]
+
+    def step():
+        B.gpt_infer_forward(ctx, flat, nxt, logits)
+        B.gpt_sample(logits, temperature, top_k, u[i[0]], nxt.view(-1))
+        i[0] += 1
+
+    ms, wall = time_steps(step, a.steps, a.warmup)
+    ids = nxt.view(-1).cpu().numpy()
+    assert ((ids >= 0) & (ids < cfg.vocab)).all() and np.isfinite(logits.cpu().numpy()).all()
+    nbytes = decode_bytes(cfg, batch, prompt + a.warmup, a.steps)
+    ach = nbytes / (ms / 1e3)
+    roof = {"bound": "hbm", "kernel": "decode step (all kernels: skinny GEMMs over every weight, "
+            "cache attention, sampling)", "achieved": round(ach / 1e9, 1), "peak": PEAK_HBM / 1e9,
+            "unit": "GB/s", "frac": round(ach / PEAK_HBM, 4), "avg_launch_ms": round(ms, 4),
+            "algorithmic_per_launch": nbytes, "traffic": None}
+    out = {"metric": "decode tokens/sec (KV-cached forward + top-k sampling) on 1 MI355X",
+           "value": round(batch / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (device-drawn N(0,0.02) weights, Zipf prompt tokens)",
+           "config": {"workload": f"{cfg.name} decode", "batch": batch, "prompt": prompt,
+                      "top_k": top_k, "temperature": temperature},
+           "prefill_ms": round(prefill_ms, 3),
+           "prefill_tokens_per_s": round(batch * prompt / (prefill_ms / 1e3), 1),
+           "wall_s": round(wall, 3), "roofline": roof}
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(cfg, flat, tok.cpu().numpy())
+    return out
+
+
+def cpu_baseline_decode(cfg, flat_dev, tokens, n_tok=96):
+    """The oracle (fp64 numpy, no cache: the full forward over the prefix) producing one next-token
+    distribution for one sequence of n_tok tokens."""
+    from threadpoolctl import threadpool_limits
+    from oracle import infer as oinf
+    cores = _cores()
+    params = inputs.unflatten(cfg, flat_dev.float().cpu().numpy())
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        z = oinf.next_logits(cfg, params, tokens[:1, :n_tok])
+        dt = time.perf_counter() - t0
+    assert np.isfinite(z).all()
+    return {"value": round(1.0 / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"next-token logits of 1 sequence after {n_tok} tokens of the {cfg.name} "
+                      f"model (fp64 numpy full forward, as the oracle has no cache), {dt:.1f} s"}
+
+
 def main():
     a = parse()
     if a.record_traffic:
@@ -633,6 +720,8 @@ def main():
         out = bench_speedrun(a, B)
     elif a.workload == "opt":
         out = bench_opt(a, B)
+    elif a.workload == "decode":
+        out = bench_decode(a, B)
     else:
         out = bench_dense(a, B)
     print(json.dumps(out), flush=True)

@@ -23,7 +23,9 @@ EXPORTS = [
     "gpt_param_layout", "gpt_workspace_bytes", "gpt_init", "gpt_fwd_bwd", "gpt_check_errors",
     "gpt_profile", "gpt_profile_read", "gpt_destroy", "bigram_fwd", "bigram_workspace_bytes", "bigram_bwd_update",
     "gpt_last_error", "gpt_status_string", "gpt_opt_state_elems", "gpt_opt_workspace_bytes",
-    "gpt_opt_step", "gpt_lr_multiplier", "gpt_muon_momentum",
+    "gpt_opt_step", "gpt_lr_multiplier", "gpt_muon_momentum", "gpt_infer_workspace_bytes",
+    "gpt_infer_init", "gpt_infer_reset", "gpt_infer_position", "gpt_infer_forward",
+    "gpt_infer_destroy", "gpt_sample",
 ]
 # Every symbol include/gpt_kernels.h declares.
 KERNEL_EXPORTS = [
@@ -106,6 +108,13 @@ def lib() -> C.CDLL:
                                    vp]),
             "gpt_lr_multiplier": (C.c_double, [i64, i64, C.c_double, C.c_double, C.c_double]),
             "gpt_muon_momentum": (C.c_double, [i64]),
+            "gpt_infer_workspace_bytes": (i32, [cfgp, i32, i32, C.POINTER(sz)]),
+            "gpt_infer_init": (i32, [cfgp, i32, i32, vp, sz, vp, C.POINTER(vp)]),
+            "gpt_infer_reset": (i32, [vp]),
+            "gpt_infer_position": (i32, [vp]),
+            "gpt_infer_forward": (i32, [vp, vp, vp, i32, i32, vp, vp]),
+            "gpt_infer_destroy": (i32, [vp]),
+            "gpt_sample": (i32, [vp, i32, i32, f32, i32, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -354,3 +363,68 @@ def gpt_lr_multiplier(it: int, num_iterations: int, warmup_ratio: float, warmdow
 
 def gpt_muon_momentum(it: int) -> float:
     return float(lib().gpt_muon_momentum(it))
+
+
+# ---------------------------------------------------------------- inference with a key/value cache
+def gpt_infer_workspace_bytes(cfg: GPTConfig, max_batch: int, max_seq: int) -> int:
+    c = make_config(cfg)
+    b = C.c_size_t(0)
+    _check(lib().gpt_infer_workspace_bytes(C.byref(c), int(max_batch), int(max_seq), C.byref(b)))
+    return b.value
+
+
+class InferContext:
+    """A gpt_infer context (key/value cache, rotary tables, activations) plus its workspace."""
+
+    def __init__(self, cfg: GPTConfig, max_batch: int, max_seq: int, stream=None):
+        import torch
+        self.cfg = cfg
+        self._c = make_config(cfg)
+        nbytes = gpt_infer_workspace_bytes(cfg, max_batch, max_seq)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+        h = C.c_void_p()
+        _check(lib().gpt_infer_init(C.byref(self._c), int(max_batch), int(max_seq),
+                                    self.workspace.data_ptr(), nbytes, _stream(stream),
+                                    C.byref(h)))
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            _check(lib().gpt_infer_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def gpt_infer_init(cfg: GPTConfig, max_batch: int, max_seq: int, stream=None) -> InferContext:
+    return InferContext(cfg, max_batch, max_seq, stream)
+
+
+def gpt_infer_reset(ctx: InferContext):
+    _check(lib().gpt_infer_reset(ctx.handle))
+
+
+def gpt_infer_position(ctx: InferContext) -> int:
+    return int(lib().gpt_infer_position(ctx.handle))
+
+
+def gpt_infer_forward(ctx: InferContext, params, tokens, logits, stream=None):
+    """tokens: int32 [B, T] on the device; logits: fp32 [B, V], written."""
+    B, T = tokens.shape
+    _check(lib().gpt_infer_forward(ctx.handle, _ptr(params), _ptr(tokens), B, T, _ptr(logits),
+                                   _stream(stream)))
+
+
+def gpt_infer_destroy(ctx: InferContext):
+    ctx.close()
+
+
+def gpt_sample(logits, temperature: float, top_k: int, uniforms, tokens, stream=None):
+    """logits fp32 [B, V]; uniforms fp32 [B] in [0, 1) (unused at temperature 0); tokens int32 [B]."""
+    B, V = logits.shape
+    _check(lib().gpt_sample(_ptr(logits), B, V, float(temperature), int(top_k), _ptr(uniforms),
+                            _ptr(tokens), _stream(stream)))

@@ -275,7 +275,8 @@ struct EpiAddRows {
 enum GemmSite {
   G_TEST = 0, G_QKV, G_OUT, G_UP, G_DOWN, G_HEAD, G_HEAD_DGRAD, G_HEAD_WGRAD, G_DOWN_DGRAD,
   G_DOWN_WGRAD, G_UP_DGRAD, G_UP_WGRAD, G_OUT_DGRAD, G_OUT_WGRAD, G_QKV_DGRAD, G_QKV_WGRAD,
-  G_TRI, G_TRI_WGRAD, G_NS_GRAM, G_NS_POLY, G_NS_APPLY
+  G_TRI, G_TRI_WGRAD, G_NS_GRAM, G_NS_POLY, G_NS_APPLY, G_INF_QKV, G_INF_OUT, G_INF_UP,
+  G_INF_DOWN, G_INF_HEAD
 };
 
 namespace gemm_detail {

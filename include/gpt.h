@@ -199,6 +199,44 @@ double gpt_lr_multiplier(int64_t it, int64_t num_iterations, double warmup_ratio
                          double warmdown_ratio, double final_lr_frac);
 double gpt_muon_momentum(int64_t it);
 
+/* ---- Inference with a key/value cache (GPT.forward with kv_cache and GPT.generate on the
+ * nanochat page).  A context holds the rotary tables and, per layer, the keys (after rotary and
+ * QK-norm) and values of up to max_batch sequences of max_seq positions.
+ * gpt_infer_forward appends a chunk of T tokens to every sequence (cache positions p .. p+T-1,
+ * p = gpt_infer_position): query p+t attends to cache positions 0 .. p+t (the page's full causal
+ * pass, single query over the cache, and chunk after a prefix are its special cases).  It writes
+ * the softcapped logits of each sequence's last position, fp32 [B, V], and advances the position.
+ * Arguments (device pointers unless stated): params = the flat parameter buffer of
+ * gpt_param_layout in cfg->dtype, 16-byte aligned; tokens = int32 [B, T] row-major (ids outside
+ * [0, vocab) are clamped into it, as in gpt_fwd_bwd); logits = fp32 [B, V], 16-byte aligned.
+ * The workspace (device, 256-byte aligned, gpt_infer_workspace_bytes) belongs to the caller and
+ * must outlive the context; the context itself is host memory released by gpt_infer_destroy.
+ * Work is queued on `stream` (results valid once it has run); init queues the rotary tables.
+ * Errors, with nothing queued and the position unchanged: GPT_EINVAL for null or misaligned
+ * buffers and for configs with table addends (has_x0_add, has_v_add, has_trigram must be 0),
+ * GPT_ESHAPE for B outside 1..max_batch or a batch size different from the one in use (it is
+ * fixed from the first call until gpt_infer_reset), GPT_ERANGE when p + T > max_seq,
+ * GPT_EWORKSPACE for a missing, misaligned or small workspace.  Requires max_seq <= 8192.
+ * Calls on one context must not overlap (they share its buffers). */
+typedef struct gpt_infer gpt_infer;
+gpt_status gpt_infer_workspace_bytes(const gpt_config* cfg, int32_t max_batch, int32_t max_seq,
+                                     size_t* bytes);
+gpt_status gpt_infer_init(const gpt_config* cfg, int32_t max_batch, int32_t max_seq,
+                          void* workspace, size_t ws_bytes, hipStream_t stream, gpt_infer** out);
+gpt_status gpt_infer_reset(gpt_infer* ctx);
+int32_t gpt_infer_position(const gpt_infer* ctx);
+gpt_status gpt_infer_forward(gpt_infer* ctx, const void* params, const int32_t* tokens,
+                             int32_t B, int32_t T, float* logits, hipStream_t stream);
+gpt_status gpt_infer_destroy(gpt_infer* ctx);
+/* Next-token choice per row of logits [B, V] fp32 (GPT.generate): temperature 0 -> argmax (the
+ * first of equal maxima); otherwise logits below the top_k-th largest are dropped (top_k 0 or
+ * >= V keeps all; values equal to it are kept), the rest divided by the temperature and
+ * softmaxed, and the token is the first index whose cumulative probability exceeds
+ * uniforms[b] (a caller-drawn number in [0, 1), the page's generator draw).  tokens int32 [B].
+ * Requires V <= 65536. */
+gpt_status gpt_sample(const float* logits, int32_t B, int32_t V, float temperature, int32_t top_k,
+                      const float* uniforms, int32_t* tokens, hipStream_t stream);
+
 /* Hashed n-gram gather-add (decoder-rtx bigram/trigram tables).  For each sequence b and
  * position t with current id c = tokens[b,t], previous ids p = tokens[b,t-1], pp = tokens[b,t-2]
  * (a missing previous id is `vocab`):

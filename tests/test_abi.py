@@ -162,3 +162,43 @@ def test_optimizer_step_argument_checks_without_gpu():
     zero_step = B.gpt_opt_hparams(0.02, 0.2, 0.004, 1.0, 0.95, 0.8, 0.95, 1e-10, 0.0, 1.0, 1, 5, 0)
     assert args(256, need, zero_step) == B.GPT_ERANGE             # Adam step count starts at 1
     assert L.gpt_opt_step(C.byref(c), None, None, 256, 256, C.byref(hp), 256, need, None, None) == B.GPT_EINVAL
+
+
+@pytest.mark.parametrize("cfg", [configs.TINY, configs.D32], ids=["tiny", "d32"])
+def test_inference_workspace_holds_the_cache(cfg):
+    cfg = cfg.replace(has_x0_add=0, has_v_add=0, has_trigram=0)
+    esz = 2 if cfg.dtype == B.BF16 else 4
+    b1 = B.gpt_infer_workspace_bytes(cfg, 4, 256)
+    b2 = B.gpt_infer_workspace_bytes(cfg, 4, 512)
+    cache = 2 * cfg.n_layer * 4 * cfg.n_head * 256 * cfg.head_dim * esz
+    assert b1 >= cache
+    # every buffer but the last-position ones scales with max_seq: the cache, rotary tables and
+    # per-token activations (fp32 residual, qkv, attention, MLP)
+    per_tok = (2 * cfg.n_layer * cfg.n_head * cfg.head_dim + 3 * cfg.d_model + cfg.d_mlp) * esz * 4
+    assert b2 - b1 >= 256 * per_tok
+
+
+def test_inference_argument_checks_without_gpu():
+    L = B.lib()
+    cfg = configs.TINY.replace(has_x0_add=0, has_v_add=0, has_trigram=0)
+    c = B.make_config(cfg)
+    sz = C.c_size_t(0)
+    assert L.gpt_infer_workspace_bytes(C.byref(c), 1, 8193, C.byref(sz)) == B.GPT_ESHAPE
+    assert L.gpt_infer_workspace_bytes(C.byref(c), 0, 64, C.byref(sz)) == B.GPT_ESHAPE
+    assert L.gpt_infer_workspace_bytes(C.byref(c), 1, 64, None) == B.GPT_EINVAL
+    need = B.gpt_infer_workspace_bytes(cfg, 2, 64)
+    h = C.c_void_p()
+    assert L.gpt_infer_init(C.byref(c), 2, 64, None, need, None, C.byref(h)) == B.GPT_EWORKSPACE
+    assert L.gpt_infer_init(C.byref(c), 2, 64, 256, need - 1, None, C.byref(h)) == B.GPT_EWORKSPACE
+    assert L.gpt_infer_init(C.byref(c), 2, 64, 4100, need, None, C.byref(h)) == B.GPT_EWORKSPACE
+    tables = B.make_config(configs.TINY.replace(has_x0_add=1))
+    assert L.gpt_infer_init(C.byref(tables), 2, 64, 256, 1 << 40, None, C.byref(h)) == B.GPT_EINVAL
+    assert L.gpt_infer_position(None) == -1
+    assert L.gpt_infer_reset(None) == B.GPT_EINVAL
+    assert L.gpt_infer_forward(None, 256, 256, 1, 1, 256, None) == B.GPT_EINVAL
+    assert L.gpt_sample(None, 0, 10, 1.0, 0, None, None, None) == B.GPT_OK          # empty batch
+    assert L.gpt_sample(256, 1, 0, 1.0, 0, 256, 256, None) == B.GPT_ESHAPE
+    assert L.gpt_sample(256, 1, 65537, 1.0, 0, 256, 256, None) == B.GPT_ESHAPE
+    assert L.gpt_sample(256, 1, 10, -1.0, 0, 256, 256, None) == B.GPT_ERANGE
+    assert L.gpt_sample(256, 1, 10, 1.0, -2, 256, 256, None) == B.GPT_ERANGE
+    assert L.gpt_sample(256, 1, 10, 1.0, 0, None, 256, None) == B.GPT_EINVAL       # no uniforms
