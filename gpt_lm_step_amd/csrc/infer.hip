@@ -292,7 +292,7 @@ __global__ void attn_combine_kernel(const float* __restrict__ part, T* __restric
 // m = l % 32 and, in registers 4q..4q+3, columns q*8 + (l/32)*4 + 0..3 (rows m >= M are zero
 // operands).  The waves' sums meet in LDS in a fixed order.  With S > 1 splits the epilogue is
 // EpiSplit (split y writes its own fp32 partial) and the consumer adds the partials in order.
-constexpr int SK_WAVES = 8, SK_CHUNK = 16, SK_MAX_SPLITS = 8, SK_MAX_M = 32;
+constexpr int SK_WAVES = 8, SK_CHUNK = 16, SK_MAX_SPLITS = 4, SK_MAX_M = 32;
 constexpr int SK_LDS_A = 64 * 1024;  // bytes for the staged activations
 template <class Epi>
 __global__ __launch_bounds__(SK_WAVES * WAVE) void skinny_gemm_kernel(const bf16* __restrict__ A,
