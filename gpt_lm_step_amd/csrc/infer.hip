@@ -545,6 +545,12 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_kernel(const float* __r
 #pragma unroll
     for (int i = 0; i < PER; ++i) key[i] = c0 + i < V ? key[i] : 0u;
   }
+  // phase boundary: the keys count as rewritten, so no per-column compare result (a 64-bit
+  // mask each) is carried from one phase into the next
+  auto fence_keys = [&]() {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) asm volatile("" : "+v"(key[i]));
+  };
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
   if (!(temperature > 0.f)) {
     // argmax, first index among equal maxima
@@ -582,6 +588,7 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_kernel(const float* __r
     }
   }
   tau = max(tau, fkey(-INFINITY) + 1u);
+  fence_keys();
   // softmax of the kept logits / temperature
   const float inv_t = 1.f / temperature;
   uint32_t kmax = 0;
@@ -593,8 +600,15 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_kernel(const float* __r
   __syncthreads();
   for (int i = 0; i < SAMPLE_THREADS / WAVE; ++i) kmax = max(kmax, km[i]);
   const float M = fkey_inv(kmax) * inv_t;
+  fence_keys();
   // exp of a kept column, 0 for the others (recomputed where needed to keep registers low)
-  auto ex = [&](int i) { return key[i] >= tau ? __expf(fkey_inv(key[i]) * inv_t - M) : 0.f; };
+  // (branch-free: the exp is taken for every column and the compare only selects; a padding
+  // key's NaN and a dropped column's value are discarded by the select)
+  auto ex = [&](int i) {
+    float e = __expf(fkey_inv(key[i]) * inv_t - M);
+    asm volatile("" : "+v"(e));  // keeps the compiler from turning the select into a branch
+    return key[i] >= tau ? e : 0.f;
+  };
   float mine = 0.f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) mine += ex(i);
@@ -621,8 +635,7 @@ __global__ __launch_bounds__(SAMPLE_THREADS) void sample_kernel(const float* __r
   // last kept column when rounding of the running sum leaves none; the last kept column of the
   // row when the target rounds up to the total
   int pick = -1;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) asm volatile("" : "+v"(key[i]));  // recompute, do not keep, the exps
+  fence_keys();  // recompute, do not keep, the exps
   if (target >= start && target < end) {
     // the running sums never decrease, so the first one above the target follows the count of
     // those at or below it (that column's exp is > 0)
