@@ -371,7 +371,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 8 ? 1 : 2) void attn_fwd_kernel(
     }
     __syncthreads();
   }
-  if (q0 >= Tn) return;
+  if (q >= Tn) return;  // per lane: a last wave past a length that is not a multiple of 32
   T* dst = out + ((long long)b * Tn + q) * D + h * HD;
   store_acc_rows<T, HD>(dst, o, 1.f / l, g);
   if (g == 0) lse2[((long long)b * H + h) * Tn + q] = m * sl2 + log2f(l);

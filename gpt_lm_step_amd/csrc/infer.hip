@@ -83,85 +83,11 @@ __global__ __launch_bounds__(256) void rope_append_kernel(T* __restrict__ qkv,
   store8(vc + vslot, load8(row + 2 * D + p));
 }
 
-// One workgroup per (sequence, head, query): query (b, t) at position p0 + t over cache positions
-// 0 .. p0 + t.  Scores into LDS (one key per thread), then exp(s - max), then each wave sums p V
-// over every fourth key with the lanes on the head dimensions (coalesced rows), combined in LDS.
-template <typename T, int HD>
-__global__ __launch_bounds__(256) void attn_cache_kernel(const T* __restrict__ qkv,
-                                                         const T* __restrict__ kc,
-                                                         const T* __restrict__ vc,
-                                                         T* __restrict__ out, int Tn, int H,
-                                                         int p0, int max_seq, float scale) {
-  extern __shared__ float sh[];
-  constexpr int NW = 4, DPL = HD >= WAVE ? HD / WAVE : 1;  // head dims per lane
-  float* qs = sh;                 // [HD]
-  float* red = qs + HD;           // [NW * HD] wave partials, reused for block reductions
-  float* sc = red + NW * HD;      // [p0 + Tn] scores
-  const int D = H * HD;
-  const int bh = blockIdx.x, b = bh / H, h = bh % H, t = blockIdx.y;
-  const int nk = p0 + t + 1;
-  const long long tok = (long long)b * Tn + t;
-  const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE;
-  if (threadIdx.x < HD) qs[threadIdx.x] = to_f32(qkv[tok * 3 * D + h * HD + threadIdx.x]);
-  __syncthreads();
-  const T* K = kc + ((long long)b * H + h) * max_seq * HD;
-  const T* V = vc + ((long long)b * H + h) * max_seq * HD;
-  float m = -INFINITY;
-  for (int j = threadIdx.x; j < nk; j += blockDim.x) {
-    float s = 0.f;
-#pragma unroll
-    for (int d = 0; d < HD; d += 8) {
-      float k8[8];
-      load8_f32(K + (long long)j * HD + d, k8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s += qs[d + e] * k8[e];
-    }
-    s *= scale;
-    sc[j] = s;
-    m = fmaxf(m, s);
-  }
-  m = wave_max(m);
-  if (lane == 0) red[w] = m;
-  __syncthreads();
-  float M = red[0];
-  for (int i = 1; i < NW; ++i) M = fmaxf(M, red[i]);
-  __syncthreads();
-  float ssum = 0.f;
-  for (int j = threadIdx.x; j < nk; j += blockDim.x) {
-    const float e = __expf(sc[j] - M);
-    sc[j] = e;
-    ssum += e;
-  }
-  ssum = wave_sum(ssum);
-  __syncthreads();
-  if (lane == 0) red[w] = ssum;
-  __syncthreads();
-  float S = 0.f;
-  for (int i = 0; i < NW; ++i) S += red[i];
-  __syncthreads();
-  float o[DPL] = {};
-  if (lane * DPL < HD) {
-    for (int j = w; j < nk; j += NW) {
-      const float p = sc[j];
-#pragma unroll
-      for (int k = 0; k < DPL; ++k) o[k] += p * to_f32(V[(long long)j * HD + lane * DPL + k]);
-    }
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) red[w * HD + lane * DPL + k] = o[k];
-  }
-  __syncthreads();
-  if (threadIdx.x < HD) {
-    float acc = 0.f;
-    for (int i = 0; i < NW; ++i) acc += red[i * HD + threadIdx.x];
-    out[tok * D + h * HD + threadIdx.x] = from_f32<T>(acc / S);
-  }
-}
-
-// Attention of a few new queries over the cache, split over the keys: workgroup (b H + h, t, s)
-// takes keys [s AS_KEYS, (s + 1) AS_KEYS) of query (b, t) (those at positions <= p0 + t) and
-// writes the split's running max m, sum l = sum exp(score - m) and unnormalised output
-// o = sum exp(score - m) v to part[(((b H + h) Tn + t) S + s)][HD + 2]; attn_combine_kernel
-// merges the splits.  HD / 8 lanes share a key row (8 elements each), so each load instruction
+// Attention of up to AS_MAX_T new queries over the cache, split over the keys: workgroup
+// (b H + h, u, s) takes keys [s AS_KEYS, (s + 1) AS_KEYS) of query (b, t = t0 + u) (those at
+// positions <= p0 + t) and writes the split's running max m, sum l = sum exp(score - m) and
+// unnormalised output o = sum exp(score - m) v to part[(((b H + h) Tq + u) S + s)][HD + 2]
+// (Tq = gridDim.y queries from t0 of the chunk's Tn); attn_combine_kernel merges the splits.  HD / 8 lanes share a key row (8 elements each), so each load instruction
 // of a wave covers WAVE * 8 / HD whole rows, contiguous in the cache; a wave issues the loads of
 // all its key and value rows at once (keys past the visible range load the last visible row and
 // get weight 0).
@@ -171,17 +97,17 @@ __global__ __launch_bounds__(AS_THREADS) void attn_split_kernel(const T* __restr
                                                                 const T* __restrict__ kc,
                                                                 const T* __restrict__ vc,
                                                                 float* __restrict__ part, int Tn,
-                                                                int H, int p0, int max_seq, int S,
-                                                                float scale) {
+                                                                int t0, int H, int p0, int max_seq,
+                                                                int S, float scale) {
   constexpr int LPK = HD / 8, KPI = WAVE / LPK, NW = AS_THREADS / WAVE, KW = AS_KEYS / NW;
   constexpr int NR = KW / KPI;  // rows per lane
   static_assert(KW % KPI == 0 && AS_KEYS <= AS_THREADS, "key split shape");
   __shared__ float qs[HD], sc[AS_KEYS], red[NW * HD], wm[NW], wl[NW];
-  const int bh = blockIdx.x, b = bh / H, h = bh % H, t = blockIdx.y, sp = blockIdx.z;
+  const int bh = blockIdx.x, b = bh / H, h = bh % H, u = blockIdx.y, t = t0 + u, sp = blockIdx.z;
   const int k0 = sp * AS_KEYS, k1 = min(p0 + t + 1, k0 + AS_KEYS);
   const int D = H * HD;
   const long long tok = (long long)b * Tn + t;
-  float* out = part + (((long long)bh * Tn + t) * S + sp) * (HD + 2);
+  float* out = part + (((long long)bh * gridDim.y + u) * S + sp) * (HD + 2);
   if (k0 >= k1) {  // no key of this split is visible to the query
     if (threadIdx.x < HD) out[threadIdx.x] = 0.f;
     if (threadIdx.x == 0) { out[HD] = -INFINITY; out[HD + 1] = 0.f; }
@@ -260,11 +186,11 @@ __global__ __launch_bounds__(AS_THREADS) void attn_split_kernel(const T* __restr
   }
 }
 
-// out[b, t, h, :] = sum_s exp(m_s - M) o_s / sum_s exp(m_s - M) l_s, M = max_s m_s (splits in
-// order); one workgroup per (b H + h, t), one thread per head dimension.
+// out[b, t0 + u, h, :] = sum_s exp(m_s - M) o_s / sum_s exp(m_s - M) l_s, M = max_s m_s
+// (splits in order); one workgroup per (b H + h, u), u < Tq, one thread per head dimension.
 template <typename T>
 __global__ void attn_combine_kernel(const float* __restrict__ part, T* __restrict__ out, int Tn,
-                                    int H, int hd, int S) {
+                                    int t0, int Tq, int H, int hd, int S) {
   const int q = blockIdx.x, d = threadIdx.x;
   if (d >= hd) return;
   const float* p = part + (long long)q * S * (hd + 2);
@@ -277,7 +203,7 @@ __global__ void attn_combine_kernel(const float* __restrict__ part, T* __restric
     L += wgt * p[s * (hd + 2) + hd + 1];
     acc += wgt * p[s * (hd + 2) + d];
   }
-  const int bh = q / Tn, t = q % Tn, b = bh / H, h = bh % H;
+  const int bh = q / Tq, t = t0 + q % Tq, b = bh / H, h = bh % H;
   out[((long long)b * Tn + t) * H * hd + h * hd + d] = from_f32<T>(acc / L);
 }
 
@@ -730,23 +656,20 @@ gpt_status infer_forward(gpt_infer* c, const T* P, const int32_t* tokens, int B,
     rope_append_kernel<T><<<cdiv(M * D / 8, 256), 256, 0, s>>>(qkv, cos_t, sin_t, kc, vc, B, Tn, H,
                                                                 hd, p0, c->max_seq, g.qk_norm,
                                                                 g.rms_eps);
-    if (p0 == 0 && Tn % 64 == 0) {
+    if (p0 == 0 && Tn > AS_MAX_T) {
+      // a first chunk: the training kernel's causal pass over the chunk itself
       TRY(launch_attn_fwd<T>(qkv, att, c->lse2, B, Tn, H, hd, s));
-    } else if (Tn <= AS_MAX_T) {
-      const int S = cdiv(p0 + Tn, AS_KEYS);
-      const float scale = 1.f / sqrtf((float)hd);
-      dim3 grid(B * H, Tn, S);
-      if (hd == 128) attn_split_kernel<T, 128><<<grid, AS_THREADS, 0, s>>>(qkv, kc, vc, c->part, Tn, H, p0, c->max_seq, S, scale);
-      else if (hd == 64) attn_split_kernel<T, 64><<<grid, AS_THREADS, 0, s>>>(qkv, kc, vc, c->part, Tn, H, p0, c->max_seq, S, scale);
-      else attn_split_kernel<T, 32><<<grid, AS_THREADS, 0, s>>>(qkv, kc, vc, c->part, Tn, H, p0, c->max_seq, S, scale);
-      attn_combine_kernel<T><<<B * H * Tn, 128, 0, s>>>(c->part, att, Tn, H, hd, S);
     } else {
-      const size_t lds = (size_t)(hd + 4 * hd + p0 + Tn) * sizeof(float);
+      // queries over the cache, AS_MAX_T at a time
       const float scale = 1.f / sqrtf((float)hd);
-      dim3 grid(B * H, Tn);
-      if (hd == 128) attn_cache_kernel<T, 128><<<grid, 256, lds, s>>>(qkv, kc, vc, att, Tn, H, p0, c->max_seq, scale);
-      else if (hd == 64) attn_cache_kernel<T, 64><<<grid, 256, lds, s>>>(qkv, kc, vc, att, Tn, H, p0, c->max_seq, scale);
-      else attn_cache_kernel<T, 32><<<grid, 256, lds, s>>>(qkv, kc, vc, att, Tn, H, p0, c->max_seq, scale);
+      for (int t0 = 0; t0 < Tn; t0 += AS_MAX_T) {
+        const int tq = std::min(AS_MAX_T, Tn - t0), S = cdiv(p0 + t0 + tq, AS_KEYS);
+        const dim3 grid(B * H, tq, S);
+        if (hd == 128) attn_split_kernel<T, 128><<<grid, AS_THREADS, 0, s>>>(qkv, kc, vc, c->part, Tn, t0, H, p0, c->max_seq, S, scale);
+        else if (hd == 64) attn_split_kernel<T, 64><<<grid, AS_THREADS, 0, s>>>(qkv, kc, vc, c->part, Tn, t0, H, p0, c->max_seq, S, scale);
+        else attn_split_kernel<T, 32><<<grid, AS_THREADS, 0, s>>>(qkv, kc, vc, c->part, Tn, t0, H, p0, c->max_seq, S, scale);
+        attn_combine_kernel<T><<<B * H * tq, 128, 0, s>>>(c->part, att, Tn, t0, tq, H, hd, S);
+      }
     }
     if (dec) {
       TRY(skinny_resid_rms<T>(c, (int)M, D, D, att, P + L.wo[l], a, s));

@@ -63,15 +63,16 @@ def _check_logits(got, want, bf16):
     (BF16_HD128, [64, 1, 5, 1]),
     (BF16_SMALL, [320, 1, 3, 1]),                    # decode over two key splits
     (configs.TINY, [64, 200, 1, 16]),                # long chunk after a prefix, then splits
+    (configs.TINY, [45, 3, 1]),                      # first chunk not a multiple of 32
 ], ids=["fp32-chunks", "fp32-prefill64", "bf16-prefill128", "bf16-ragged", "bf16-hd128",
-        "bf16-two-splits", "fp32-long-chunk"])
+        "bf16-two-splits", "fp32-long-chunk", "fp32-ragged-prefill"])
 def test_chunked_inference_matches_the_full_forward(cfg, chunks):
     """Logits after every chunk equal the oracle's full forward over the whole prefix: one
     oracle pass gives every position's logits (causality is pinned in the oracle's tests).  The
-    chunks cover each attention path: the full causal kernel (a first chunk of a multiple of 64
-    tokens), the key-split kernel (chunks of up to 16 tokens, one or more splits of 256 keys) and
-    the per-query kernel (longer chunks after a prefix); bf16 chunks of up to 32 tokens in all
-    take the decode GEMM."""
+    chunks cover each attention path: the causal kernel of training (first chunks of more than 16
+    tokens, including lengths that are not a multiple of 32) and the key-split kernel (first
+    chunks of up to 16 tokens, every later chunk in groups of 16 queries, one or more splits of
+    128 keys); bf16 chunks of up to 32 tokens in all take the decode GEMM."""
     params, flat = _model(cfg, 201)
     n = sum(chunks)
     tok = inputs.uniform_tokens(7, (3, n + 1), cfg.vocab)
