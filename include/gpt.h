@@ -211,7 +211,8 @@ double gpt_muon_momentum(int64_t it);
  * [0, vocab) are clamped into it, as in gpt_fwd_bwd); logits = fp32 [B, V], 16-byte aligned.
  * The workspace (device, 256-byte aligned, gpt_infer_workspace_bytes) belongs to the caller and
  * must outlive the context; the context itself is host memory released by gpt_infer_destroy.
- * Work is queued on `stream` (results valid once it has run); init queues the rotary tables.
+ * Work is queued on `stream` (results valid once it has run); init queues the rotary tables on
+ * its stream, so work on another stream must be ordered after it by the caller.
  * Errors, with nothing queued and the position unchanged: GPT_EINVAL for null or misaligned
  * buffers and for configs with table addends (has_x0_add, has_v_add, has_trigram must be 0),
  * GPT_ESHAPE for B outside 1..max_batch or a batch size different from the one in use (it is
