@@ -212,6 +212,14 @@ def _roof_entry(name, calls, tot_ms, flops, nbytes, bf16):
             "avg_launch_ms": round(per_launch_s * 1e3, 4), "algorithmic_per_launch": nbytes / calls}
 
 
+def _roof_entry_by_intensity(name, calls, tot_ms, flops, nbytes):
+    """Roofline of a bf16 stage bound by whichever resource its arithmetic intensity selects:
+    the matrix cores above the ridge (peak FLOP/s / peak bytes/s), HBM below it."""
+    if flops > 0 and flops / max(nbytes, 1.0) >= PEAK_BF16 / PEAK_HBM:
+        return _roof_entry(name, calls, tot_ms, flops, nbytes, True)
+    return _roof_entry(name, calls, tot_ms, 0.0, nbytes, True)
+
+
 def profile_stages(B, ctx, step, n_steps, bf16, multi=frozenset(), workload=None):
     """Instrumented pass: every launch bracketed by events on the step's stream.  Returns the
     dominant single-kernel stage's roofline and a per-stage table."""
@@ -632,10 +640,11 @@ def bench_decode(a, B):
     batch, prompt, top_k, temperature = 8, 1024, 50, 1.0
     seeds = inputs.seeds_for(cfg.name)
     flat = inputs.device_params(cfg, seeds["weights"])
-    max_seq = prompt + a.warmup + a.steps
+    prof_steps = max(a.profile_steps, 1)
+    max_seq = prompt + a.warmup + a.steps + prof_steps
     ctx = B.gpt_infer_init(cfg, batch, max_seq)
     g = torch.Generator(device="cuda").manual_seed(seeds["tokens"])
-    u = torch.rand(a.warmup + a.steps + 1, batch, device="cuda", generator=g)
+    u = torch.rand(a.warmup + a.steps + prof_steps + 1, batch, device="cuda", generator=g)
     tok = torch.from_numpy(inputs.zipf_tokens(seeds["tokens"], (batch, prompt), cfg.vocab)).cuda()
     logits = torch.empty(batch, cfg.vocab, device="cuda")
     nxt = torch.empty(batch, 1, dtype=torch.int32, device="cuda")
@@ -659,10 +668,25 @@ def bench_decode(a, B):
     assert ((ids >= 0) & (ids < cfg.vocab)).all() and np.isfinite(logits.cpu().numpy()).all()
     nbytes = decode_bytes(cfg, batch, prompt + a.warmup, a.steps)
     ach = nbytes / (ms / 1e3)
-    roof = {"bound": "hbm", "kernel": "decode step (all kernels: skinny GEMMs over every weight, "
-            "cache attention, sampling)", "achieved": round(ach / 1e9, 1), "peak": PEAK_HBM / 1e9,
-            "unit": "GB/s", "frac": round(ach / PEAK_HBM, 4), "avg_launch_ms": round(ms, 4),
-            "algorithmic_per_launch": nbytes, "traffic": None}
+    step_roof = {"bound": "hbm", "kernel": "decode step (all kernels)", "achieved": round(ach / 1e9, 1),
+                 "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": round(ach / PEAK_HBM, 4),
+                 "algorithmic_per_step": nbytes}
+    # instrumented pass: every launch of a few more steps bracketed by events on the stream
+    B.gpt_infer_profile(ctx, True)
+    for _ in range(prof_steps):
+        step()
+    B.gpt_infer_profile(ctx, False)
+    stages = B.gpt_infer_profile_read(ctx)
+    torch.cuda.synchronize()
+    parts = {}
+    for n, c, m, f, b in stages:
+        e = _roof_entry_by_intensity(n, c, m, f, b)
+        parts[n] = {"ms_per_step": round(m / prof_steps, 4), "launches": c // prof_steps,
+                    "achieved": e["achieved"], "unit": e["unit"], "frac": e["frac"]}
+    name, calls, tot_ms, flops, nb = max(stages, key=lambda x: x[2])
+    roof = _roof_entry_by_intensity(name, calls, tot_ms, flops, nb)
+    roof["traffic"] = None
+    roof["launches_per_step"] = calls // prof_steps
     out = {"metric": "decode tokens/sec (KV-cached forward + top-k sampling) on 1 MI355X",
            "value": round(batch / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
@@ -672,7 +696,7 @@ def bench_decode(a, B):
                       "top_k": top_k, "temperature": temperature},
            "prefill_ms": round(prefill_ms, 3),
            "prefill_tokens_per_s": round(batch * prompt / (prefill_ms / 1e3), 1),
-           "wall_s": round(wall, 3), "roofline": roof}
+           "wall_s": round(wall, 3), "roofline": roof, "step_roofline": step_roof, "parts": parts}
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(cfg, flat, tok.cpu().numpy())
     return out

@@ -3,6 +3,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 
 #include "kernels.h"
@@ -21,6 +22,34 @@ gpt_status fail(gpt_status s, const std::string& msg) {
 gpt_status check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GPT_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+  return GPT_OK;
+}
+
+gpt_status prof_read(Prof& pr, gpt_profile_entry* out, int32_t* count, const char* who) {
+  std::vector<gpt_profile_entry> agg;
+  for (const ProfRec& r : pr.recs) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return fail(GPT_EHIP, std::string(who) + ": event sync failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return fail(GPT_EHIP, std::string(who) + ": elapsed failed");
+    gpt_profile_entry* e = nullptr;
+    for (auto& x : agg)
+      if (strcmp(x.name, r.name) == 0) e = &x;
+    if (!e) {
+      agg.push_back(gpt_profile_entry{});
+      e = &agg.back();
+      snprintf(e->name, sizeof(e->name), "%s", r.name);
+    }
+    e->calls += 1;
+    e->ms += ms;
+    e->flops += r.flops;
+    e->bytes += r.bytes;
+  }
+  pr.recs.clear();
+  pr.next = 0;
+  const int32_t cap = *count;
+  *count = (int32_t)agg.size();
+  if (out)
+    for (int32_t i = 0; i < std::min(cap, *count); ++i) out[i] = agg[i];
   return GPT_OK;
 }
 

@@ -23,6 +23,7 @@ struct gpt_infer {
   float* sk_part;  // skinny-GEMM split partials [splits][M][d_model], M <= SK_MAX_M
   int32_t* tok_c;
   int* err;
+  gpt::Prof prof;  // per-launch timing (gpt_infer_profile)
 };
 
 namespace gpt {
@@ -393,23 +394,28 @@ __global__ __launch_bounds__(256) void resid_rms_kernel(float* __restrict__ x,
   }
 }
 
-// x += A W^T followed by y = RMSNorm(x) for a decode-sized product: split partials from the
-// skinny kernel, then resid_rms_kernel.
+// x += A W^T followed by y = RMSNorm(x) for a decode-sized product, in two launches: the skinny
+// kernel's split partials (skinny_split, which returns the split count), then resid_rms_kernel.
 template <typename T>
-gpt_status skinny_resid_rms(gpt_infer* c, int M, int N, int K, const T* A, const T* W, T* y,
-                            hipStream_t s) {
+gpt_status skinny_split(gpt_infer* c, int M, int N, int K, const T* A, const T* W, int* S_out,
+                        hipStream_t s) {
   if constexpr (!std::is_same<T, bf16>::value) {
     return fail(GPT_EINVAL, "skinny gemm: bf16 only");
   } else {
-  const int S = skinny_splits(M, N, K);
-  if (S < 1 || !skinny_ok(M, N, K, K, K, S) ||
-      (long long)S * M * N > (long long)SK_MAX_SPLITS * SK_MAX_M * c->cfg.d_model)
-    return fail(GPT_EINVAL, "skinny gemm: no split of K fits");
-  skinny_gemm_kernel<<<dim3(N / 32, S), SK_WAVES * WAVE, skinny_lds(M, K, S), s>>>(
-      A, K, M, W, K, K, EpiSplit{c->sk_part, (long long)M * N, (long long)N});
-  resid_rms_kernel<bf16><<<M, 256, 0, s>>>(c->x, c->sk_part, S, y, c->rstd, M, N, c->cfg.rms_eps);
-  return check_launch("skinny gemm + residual rmsnorm");
+    const int S = skinny_splits(M, N, K);
+    if (S < 1 || !skinny_ok(M, N, K, K, K, S) ||
+        (long long)S * M * N > (long long)SK_MAX_SPLITS * SK_MAX_M * c->cfg.d_model)
+      return fail(GPT_EINVAL, "skinny gemm: no split of K fits");
+    skinny_gemm_kernel<<<dim3(N / 32, S), SK_WAVES * WAVE, skinny_lds(M, K, S), s>>>(
+        A, K, M, W, K, K, EpiSplit{c->sk_part, (long long)M * N, (long long)N});
+    *S_out = S;
+    return check_launch("skinny gemm (split)");
   }
+}
+template <typename T>
+gpt_status resid_rms(gpt_infer* c, int M, int N, int S, T* y, hipStream_t s) {
+  resid_rms_kernel<T><<<M, 256, 0, s>>>(c->x, c->sk_part, S, y, c->rstd, M, N, c->cfg.rms_eps);
+  return check_launch("residual + rmsnorm");
 }
 
 // xl[b] = x[b * Tn + Tn - 1]: the residual stream at each sequence's last position.
@@ -637,60 +643,123 @@ gpt_status infer_forward(gpt_infer* c, const T* P, const int32_t* tokens, int B,
   const T* cos_t = (const T*)c->cos_t + (long long)p0 * hd / 2;
   const T* sin_t = (const T*)c->sin_t + (long long)p0 * hd / 2;
   const long long layer_cache = (long long)c->max_batch * H * c->max_seq * hd;
+  const double es = sizeof(T), Md = (double)M;
+  Prof& prof = c->prof;
+  // one launch (or a loop of one kind of launch); with profiling on, bracketed by events and
+  // tagged with its algorithmic work: flops of its products, bytes it must move once
+  auto run = [&](const char* name, double flops, double bytes, auto&& fn) -> gpt_status {
+    if (!prof.on) return fn();
+    hipEvent_t e0 = prof.get(), e1 = prof.get();
+    if (!e0 || !e1) return fail(GPT_EHIP, "profiling: hipEventCreate failed");
+    (void)hipEventRecord(e0, s);
+    gpt_status st = fn();
+    (void)hipEventRecord(e1, s);
+    prof.recs.push_back({name, flops, bytes, e0, e1});
+    return st;
+  };
+  auto mm = [](double m, double n, double k) { return 2.0 * m * n * k; };
 #define TRY(x)                                 \
   do {                                         \
     gpt_status st_ = (x);                      \
     if (st_ != GPT_OK) return st_;             \
   } while (0)
-  TRY(launch_embed_fwd<T>(tokens, P + L.wte, nullptr, c->x, c->rstd, c->tok_c, c->err, M, D, V,
-                          g.rms_eps, s));
+  TRY(run("embed", 0, Md * D * (es + 4), [&] {
+    return launch_embed_fwd<T>(tokens, P + L.wte, nullptr, c->x, c->rstd, c->tok_c, c->err, M, D, V,
+                               g.rms_eps, s);
+  }));
   // decode-sized steps: each residual product leaves the next product's normalised input
   const bool dec = std::is_same<T, bf16>::value && skinny_splits((int)M, D, D) > 0 &&
                    skinny_splits((int)M, D, F) > 0 && D <= 256 * 8 * RR_MAXIT;
   for (int l = 0; l < g.n_layer; ++l) {
     T* kc = (T*)c->kc + l * layer_cache;
     T* vc = (T*)c->vc + l * layer_cache;
-    if (l == 0 || !dec) TRY(launch_rms_fwd<T>(c->x, a, c->rstd, M, D, g.rms_eps, s));
-    TRY((infer_gemm<G_INF_QKV, T>((int)M, 3 * D, D, a, D, P + L.wqkv[l], D,
-                                  EpiStore<T>{qkv, 3LL * D}, s)));
-    rope_append_kernel<T><<<cdiv(M * D / 8, 256), 256, 0, s>>>(qkv, cos_t, sin_t, kc, vc, B, Tn, H,
-                                                                hd, p0, c->max_seq, g.qk_norm,
-                                                                g.rms_eps);
+    if (l == 0 || !dec)
+      TRY(run("rmsnorm", 0, Md * D * (4 + es),
+              [&] { return launch_rms_fwd<T>(c->x, a, c->rstd, M, D, g.rms_eps, s); }));
+    TRY(run("qkv", mm(Md, 3.0 * D, D), (3.0 * D * D + Md * D + Md * 3 * D) * es, [&] {
+      return infer_gemm<G_INF_QKV, T>((int)M, 3 * D, D, a, D, P + L.wqkv[l], D,
+                                      EpiStore<T>{qkv, 3LL * D}, s);
+    }));
+    TRY(run("rope_append", 0, Md * 7 * D * es, [&] {
+      rope_append_kernel<T><<<cdiv(M * D / 8, 256), 256, 0, s>>>(qkv, cos_t, sin_t, kc, vc, B, Tn,
+                                                                  H, hd, p0, c->max_seq,
+                                                                  g.qk_norm, g.rms_eps);
+      return check_launch("rotary + cache append");
+    }));
     if (p0 == 0 && Tn > AS_MAX_T) {
       // a first chunk: the training kernel's causal pass over the chunk itself
-      TRY(launch_attn_fwd<T>(qkv, att, c->lse2, B, Tn, H, hd, s));
+      const double pairs = (double)B * H * Tn * (Tn + 1) / 2.0;
+      TRY(run("attention", 4.0 * pairs * hd, Md * 4 * D * es,
+              [&] { return launch_attn_fwd<T>(qkv, att, c->lse2, B, Tn, H, hd, s); }));
     } else {
       // queries over the cache, AS_MAX_T at a time
       const float scale = 1.f / sqrtf((float)hd);
       for (int t0 = 0; t0 < Tn; t0 += AS_MAX_T) {
         const int tq = std::min(AS_MAX_T, Tn - t0), S = cdiv(p0 + t0 + tq, AS_KEYS);
-        const dim3 grid(B * H, tq, S);
-        if (hd == 128) attn_split_kernel<T, 128><<<grid, AS_THREADS, 0, s>>>(qkv, kc, vc, c->part, Tn, t0, H, p0, c->max_seq, S, scale);
-        else if (hd == 64) attn_split_kernel<T, 64><<<grid, AS_THREADS, 0, s>>>(qkv, kc, vc, c->part, Tn, t0, H, p0, c->max_seq, S, scale);
-        else attn_split_kernel<T, 32><<<grid, AS_THREADS, 0, s>>>(qkv, kc, vc, c->part, Tn, t0, H, p0, c->max_seq, S, scale);
-        attn_combine_kernel<T><<<B * H * tq, 128, 0, s>>>(c->part, att, Tn, t0, tq, H, hd, S);
+        const double bh = (double)B * H, part_b = bh * tq * S * (hd + 2) * 4.0;
+        double keys = 0;  // (query, visible key) pairs of the chunk
+        for (int t = t0; t < t0 + tq; ++t) keys += p0 + t + 1;
+        TRY(run("attn_split", 4.0 * bh * keys * hd,
+                bh * (p0 + t0 + tq) * hd * 2 * es + bh * tq * hd * es + part_b, [&] {
+                  const dim3 grid(B * H, tq, S);
+                  if (hd == 128) attn_split_kernel<T, 128><<<grid, AS_THREADS, 0, s>>>(qkv, kc, vc, c->part, Tn, t0, H, p0, c->max_seq, S, scale);
+                  else if (hd == 64) attn_split_kernel<T, 64><<<grid, AS_THREADS, 0, s>>>(qkv, kc, vc, c->part, Tn, t0, H, p0, c->max_seq, S, scale);
+                  else attn_split_kernel<T, 32><<<grid, AS_THREADS, 0, s>>>(qkv, kc, vc, c->part, Tn, t0, H, p0, c->max_seq, S, scale);
+                  return check_launch("attention (key splits)");
+                }));
+        TRY(run("attn_combine", 0, part_b + bh * tq * hd * es, [&] {
+          attn_combine_kernel<T><<<B * H * tq, 128, 0, s>>>(c->part, att, Tn, t0, tq, H, hd, S);
+          return check_launch("attention (combine)");
+        }));
       }
     }
+    int S = 0;
     if (dec) {
-      TRY(skinny_resid_rms<T>(c, (int)M, D, D, att, P + L.wo[l], a, s));
+      const double sp = (double)skinny_splits((int)M, D, D);
+      TRY(run("out", mm(Md, D, D), (1.0 * D * D + Md * D) * es + sp * Md * D * 4,
+              [&] { return skinny_split<T>(c, (int)M, D, D, att, P + L.wo[l], &S, s); }));
+      TRY(run("out_resid_norm", 0, (S + 2.0) * Md * D * 4 + Md * D * es,
+              [&] { return resid_rms<T>(c, (int)M, D, S, a, s); }));
     } else {
-      TRY((infer_gemm<G_INF_OUT, T>((int)M, D, D, att, D, P + L.wo[l], D,
-                                    EpiResid{c->x, c->x, (long long)D}, s)));
-      TRY(launch_rms_fwd<T>(c->x, a, c->rstd, M, D, g.rms_eps, s));
+      TRY(run("out", mm(Md, D, D), (1.0 * D * D + Md * D) * es + 2 * Md * D * 4, [&] {
+        return infer_gemm<G_INF_OUT, T>((int)M, D, D, att, D, P + L.wo[l], D,
+                                        EpiResid{c->x, c->x, (long long)D}, s);
+      }));
+      TRY(run("rmsnorm", 0, Md * D * (4 + es),
+              [&] { return launch_rms_fwd<T>(c->x, a, c->rstd, M, D, g.rms_eps, s); }));
     }
-    TRY((infer_gemm<G_INF_UP, T>((int)M, F, D, a, D, P + L.wfc[l], D,
-                                 EpiRelu2<T>{act, (long long)F}, s)));
-    if (dec)
-      TRY(skinny_resid_rms<T>(c, (int)M, D, F, act, P + L.wpr[l], a, s));
-    else
-      TRY((infer_gemm<G_INF_DOWN, T>((int)M, D, F, act, F, P + L.wpr[l], F,
-                                     EpiResid{c->x, c->x, (long long)D}, s)));
+    TRY(run("up", mm(Md, F, D), (1.0 * F * D + Md * D + Md * F) * es, [&] {
+      return infer_gemm<G_INF_UP, T>((int)M, F, D, a, D, P + L.wfc[l], D,
+                                     EpiRelu2<T>{act, (long long)F}, s);
+    }));
+    if (dec) {
+      const double sp = (double)skinny_splits((int)M, D, F);
+      TRY(run("down", mm(Md, D, F), (1.0 * D * F + Md * F) * es + sp * Md * D * 4,
+              [&] { return skinny_split<T>(c, (int)M, D, F, act, P + L.wpr[l], &S, s); }));
+      TRY(run("down_resid_norm", 0, (S + 2.0) * Md * D * 4 + Md * D * es,
+              [&] { return resid_rms<T>(c, (int)M, D, S, a, s); }));
+    } else {
+      TRY(run("down", mm(Md, D, F), (1.0 * D * F + Md * F) * es + 2 * Md * D * 4, [&] {
+        return infer_gemm<G_INF_DOWN, T>((int)M, D, F, act, F, P + L.wpr[l], F,
+                                         EpiResid{c->x, c->x, (long long)D}, s);
+      }));
+    }
   }
-  gather_last_kernel<<<cdiv((long long)B * D, 256), 256, 0, s>>>(c->x, c->xl, B, Tn, D);
-  TRY(launch_rms_fwd<T>(c->xl, fl, c->rstd, B, D, g.rms_eps, s));
-  TRY((infer_gemm<G_INF_HEAD, T>(B, V, D, fl, D, P + L.lm_head, D,
-                                 EpiStoreF32{logits, (long long)V, 0}, s)));
-  softcap_kernel<<<cdiv((long long)B * V, 256), 256, 0, s>>>(logits, (long long)B * V, g.softcap);
+  const double Bd = B;
+  TRY(run("gather_last", 0, Bd * D * 8, [&] {
+    gather_last_kernel<<<cdiv((long long)B * D, 256), 256, 0, s>>>(c->x, c->xl, B, Tn, D);
+    return check_launch("gather last positions");
+  }));
+  TRY(run("final_norm", 0, Bd * D * (4 + es),
+          [&] { return launch_rms_fwd<T>(c->xl, fl, c->rstd, B, D, g.rms_eps, s); }));
+  TRY(run("head", mm(Bd, V, D), (1.0 * V * D + Bd * D) * es + Bd * V * 4, [&] {
+    return infer_gemm<G_INF_HEAD, T>(B, V, D, fl, D, P + L.lm_head, D,
+                                     EpiStoreF32{logits, (long long)V, 0}, s);
+  }));
+  TRY(run("softcap", 0, Bd * V * 8, [&] {
+    softcap_kernel<<<cdiv((long long)B * V, 256), 256, 0, s>>>(logits, (long long)B * V, g.softcap);
+    return check_launch("softcap");
+  }));
 #undef TRY
   return check_launch("inference forward");
 }
@@ -792,6 +861,17 @@ gpt_status gpt_sample(const float* logits, int32_t B, int32_t V, float temperatu
   else
     sample_kernel<64><<<B, SAMPLE_THREADS, 0, stream>>>(logits, V, temperature, top_k, uniforms, tokens);
   return check_launch("sample");
+}
+
+gpt_status gpt_infer_profile(gpt_infer* ctx, int32_t enable) {
+  if (!ctx) return fail(GPT_EINVAL, "gpt_infer_profile: null context");
+  ctx->prof.on = enable != 0;
+  return GPT_OK;
+}
+
+gpt_status gpt_infer_profile_read(gpt_infer* ctx, gpt_profile_entry* out, int32_t* count) {
+  if (!ctx || !count) return fail(GPT_EINVAL, "gpt_infer_profile_read: null argument");
+  return prof_read(ctx->prof, out, count, "gpt_infer_profile_read");
 }
 
 gpt_status gpt_infer_destroy(gpt_infer* ctx) {

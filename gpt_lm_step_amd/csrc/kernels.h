@@ -101,4 +101,34 @@ template <typename T>
 gpt_status launch_attn_bwd(const T* qkv, const T* out, const T* dout, const float* lse2,
                            float* dq_sum, T* dqkv, int B, int Tn, int H, int hd, hipStream_t s);
 
+// Optional per-launch timing: when enabled, every launch of a step is bracketed by two events
+// on the step's stream and tagged with its stage name and algorithmic work.
+struct ProfRec {
+  const char* name;
+  double flops, bytes;
+  hipEvent_t a, b;
+};
+struct Prof {
+  bool on = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  size_t next = 0;
+  hipEvent_t get() {
+    if (next == pool.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[next++];
+  }
+  ~Prof() {
+    for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+  }
+};
+
+// Aggregates the recorded launches by stage name (in order of first launch) after waiting for
+// their events, clears the record, and writes up to *count entries (*count: capacity in, number
+// of stages out; out may be null).  `who` names the entry point in error messages.
+gpt_status prof_read(Prof& pr, gpt_profile_entry* out, int32_t* count, const char* who);
+
 }  // namespace gpt

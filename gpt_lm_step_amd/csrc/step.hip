@@ -149,31 +149,6 @@ Plan carve_plan(const gpt_config& c, Carver& cv) {
   return p;
 }
 
-// Optional per-launch timing: when enabled, every launch of a step is bracketed by two events
-// on the step's stream and tagged with its stage name and algorithmic work.
-struct ProfRec {
-  const char* name;
-  double flops, bytes;
-  hipEvent_t a, b;
-};
-struct Prof {
-  bool on = false;
-  std::vector<ProfRec> recs;
-  std::vector<hipEvent_t> pool;
-  size_t next = 0;
-  hipEvent_t get() {
-    if (next == pool.size()) {
-      hipEvent_t e;
-      if (hipEventCreate(&e) != hipSuccess) return nullptr;
-      pool.push_back(e);
-    }
-    return pool[next++];
-  }
-  ~Prof() {
-    for (hipEvent_t e : pool) (void)hipEventDestroy(e);
-  }
-};
-
 }  // namespace
 }  // namespace gpt
 
@@ -484,32 +459,7 @@ gpt_status gpt_profile(gpt_ctx* ctx, int32_t enable) {
 
 gpt_status gpt_profile_read(gpt_ctx* ctx, gpt_profile_entry* out, int32_t* count) {
   if (!ctx || !count) return fail(GPT_EINVAL, "gpt_profile_read: null argument");
-  Prof& pr = ctx->prof;
-  std::vector<gpt_profile_entry> agg;
-  for (const ProfRec& r : pr.recs) {
-    if (hipEventSynchronize(r.b) != hipSuccess) return fail(GPT_EHIP, "gpt_profile_read: event sync failed");
-    float ms = 0.f;
-    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return fail(GPT_EHIP, "gpt_profile_read: elapsed failed");
-    gpt_profile_entry* e = nullptr;
-    for (auto& x : agg)
-      if (strcmp(x.name, r.name) == 0) e = &x;
-    if (!e) {
-      agg.push_back(gpt_profile_entry{});
-      e = &agg.back();
-      snprintf(e->name, sizeof(e->name), "%s", r.name);
-    }
-    e->calls += 1;
-    e->ms += ms;
-    e->flops += r.flops;
-    e->bytes += r.bytes;
-  }
-  pr.recs.clear();
-  pr.next = 0;
-  const int32_t cap = *count;
-  *count = (int32_t)agg.size();
-  if (out)
-    for (int32_t i = 0; i < std::min(cap, *count); ++i) out[i] = agg[i];
-  return GPT_OK;
+  return prof_read(ctx->prof, out, count, "gpt_profile_read");
 }
 
 gpt_status gpt_destroy(gpt_ctx* ctx) {

@@ -228,6 +228,14 @@ gpt_status gpt_infer_reset(gpt_infer* ctx);
 int32_t gpt_infer_position(const gpt_infer* ctx);
 gpt_status gpt_infer_forward(gpt_infer* ctx, const void* params, const int32_t* tokens,
                              int32_t B, int32_t T, float* logits, hipStream_t stream);
+/* Per-stage timing of gpt_infer_forward, as gpt_profile / gpt_profile_read for the training step:
+ * with profiling on, every launch is bracketed by two events on the call's stream and tagged with
+ * its stage (embed, rmsnorm, qkv, rope_append, attention or attn_split + attn_combine, out
+ * [+ out_resid_norm], up, down [+ down_resid_norm], gather_last, final_norm, head, softcap) and
+ * algorithmic work; the read aggregates by stage, clears the record, and fills up to *count
+ * entries [host]. */
+gpt_status gpt_infer_profile(gpt_infer* ctx, int32_t enable);
+gpt_status gpt_infer_profile_read(gpt_infer* ctx, gpt_profile_entry* out, int32_t* count);
 gpt_status gpt_infer_destroy(gpt_infer* ctx);
 /* Next-token choice per row of logits [B, V] fp32 (GPT.generate): temperature 0 -> argmax (the
  * first of equal maxima); otherwise logits below the top_k-th largest are dropped (top_k 0 or
