@@ -88,10 +88,10 @@ __global__ __launch_bounds__(256) void rope_append_kernel(T* __restrict__ qkv,
 // (b H + h, u, s) takes keys [s AS_KEYS, (s + 1) AS_KEYS) of query (b, t = t0 + u) (those at
 // positions <= p0 + t) and writes the split's running max m, sum l = sum exp(score - m) and
 // unnormalised output o = sum exp(score - m) v to part[(((b H + h) Tq + u) S + s)][HD + 2]
-// (Tq = gridDim.y queries from t0 of the chunk's Tn); attn_combine_kernel merges the splits.  HD / 8 lanes share a key row (8 elements each), so each load instruction
-// of a wave covers WAVE * 8 / HD whole rows, contiguous in the cache; a wave issues the loads of
-// all its key and value rows at once (keys past the visible range load the last visible row and
-// get weight 0).
+// (Tq = gridDim.y queries from t0 of the chunk's Tn); attn_combine_kernel merges the splits.
+// HD / 8 lanes share a key row (8 elements each), so each load instruction of a wave covers
+// WAVE * 8 / HD whole rows, contiguous in the cache; a wave issues the loads of all its key and
+// value rows at once (keys past the visible range load the last visible row and get weight 0).
 constexpr int AS_KEYS = 128, AS_THREADS = 256, AS_MAX_T = 16;
 template <typename T, int HD>
 __global__ __launch_bounds__(AS_THREADS) void attn_split_kernel(const T* __restrict__ qkv,
