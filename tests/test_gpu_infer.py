@@ -193,3 +193,29 @@ def test_draws_follow_the_inverse_cdf(V, temperature, top_k):
         if not near:
             assert g == want[r], (r, g, want[r])
     assert rows - edge >= rows // 2     # most draws are decided exactly
+
+
+def test_inference_profile_stages():
+    """gpt_infer_profile brackets every launch of a decode step: each per-layer stage appears
+    once per layer with positive time and work, and reading clears the record."""
+    cfg = BF16_SMALL
+    _, flat = _model(cfg, 204)
+    tok = inputs.uniform_tokens(12, (2, 9), cfg.vocab)
+    ctx = B.gpt_infer_init(cfg, 2, 16)
+    logits = torch.empty(2, cfg.vocab, device="cuda")
+    B.gpt_infer_forward(ctx, flat, dev(tok[:, :8]), logits)
+    B.gpt_infer_profile(ctx, True)
+    B.gpt_infer_forward(ctx, flat, dev(tok[:, 8:9]), logits)
+    B.gpt_infer_profile(ctx, False)
+    stages = {n: (c, ms, f, b) for n, c, ms, f, b in B.gpt_infer_profile_read(ctx)}
+    L = cfg.n_layer
+    per_layer = ("qkv", "rope_append", "attn_split", "attn_combine", "out", "out_resid_norm", "up",
+                 "down", "down_resid_norm")
+    for name in per_layer:
+        calls, ms, flops, nbytes = stages[name]
+        assert calls == L and ms > 0 and nbytes > 0, (name, stages[name])
+    for name in ("embed", "rmsnorm", "gather_last", "final_norm", "head", "softcap"):
+        assert stages[name][0] == 1, name
+    assert stages["qkv"][2] == 2.0 * 2 * 3 * cfg.d_model * cfg.d_model * L
+    assert B.gpt_infer_profile_read(ctx) == []
+    ctx.close()
