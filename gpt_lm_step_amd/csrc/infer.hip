@@ -51,6 +51,8 @@ __global__ __launch_bounds__(256) void rope_append_kernel(T* __restrict__ qkv,
   T* row = qkv + tok * 3 * D;
   T* base = row + (hq < H ? 0 : D) + hh * hd;
   float x1[8], x2[8], c[8], sn[8], y1[8], y2[8];
+  // every load first (v's too), so the kernel makes one round trip to memory
+  const vec8_t<T> v8 = load8(row + 2 * D + p);
   load8_f32(base + i, x1);
   load8_f32(base + i + half, x2);
   load8_f32(cos_t + t * half + i, c);
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(T* __restrict__ qkv,
   }
   // v group p of this token: head p / hd, dims p % hd .. +8
   const long long vslot = (((long long)b * H + p / hd) * max_seq + p0 + t) * hd + p % hd;
-  store8(vc + vslot, load8(row + 2 * D + p));
+  store8(vc + vslot, v8);
 }
 
 // Attention of up to AS_MAX_T new queries over the cache, split over the keys: workgroup
@@ -195,9 +197,12 @@ __global__ void attn_combine_kernel(const float* __restrict__ part, T* __restric
   const int q = blockIdx.x, d = threadIdx.x;
   if (d >= hd) return;
   const float* p = part + (long long)q * S * (hd + 2);
+  // (unrolled so that a group of splits' loads is in flight together)
   float M = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < S; ++s) M = fmaxf(M, p[s * (hd + 2) + hd]);
   float L = 0.f, acc = 0.f;
+#pragma unroll 8
   for (int s = 0; s < S; ++s) {
     const float ms = p[s * (hd + 2) + hd];
     const float wgt = ms == -INFINITY ? 0.f : __expf(ms - M);
