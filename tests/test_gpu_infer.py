@@ -64,8 +64,9 @@ def _check_logits(got, want, bf16):
     (BF16_SMALL, [320, 1, 3, 1]),                    # decode over two key splits
     (configs.TINY, [64, 200, 1, 16]),                # long chunk after a prefix, then splits
     (configs.TINY, [45, 3, 1]),                      # first chunk not a multiple of 32
+    (BF16_SMALL, [40, 8, 10]),                       # 24 and 30 token rows on the decode GEMM
 ], ids=["fp32-chunks", "fp32-prefill64", "bf16-prefill128", "bf16-ragged", "bf16-hd128",
-        "bf16-two-splits", "fp32-long-chunk", "fp32-ragged-prefill"])
+        "bf16-two-splits", "fp32-long-chunk", "fp32-ragged-prefill", "bf16-wide-decode"])
 def test_chunked_inference_matches_the_full_forward(cfg, chunks):
     """Logits after every chunk equal the oracle's full forward over the whole prefix: one
     oracle pass gives every position's logits (causality is pinned in the oracle's tests).  The
