@@ -65,6 +65,7 @@ TRAFFIC_KERNELS = {
     "attn_bwd_dkdv": ("attn_bwd_dkdv_pipe_kernel", "attn.hip"),
     "softcap_ce": ("9ce_kernelI|::ce_kernel<", "ce.hip"),
     "bigram_fwd (hash + gather-add, x0 table)": ("bigram_gather_kernel", "tables.hip"),
+    "attn_split": ("attn_split_kernel", "infer.hip"),
 }
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gpt_lm_step_amd", "csrc")
@@ -685,7 +686,7 @@ def bench_decode(a, B):
                     "achieved": e["achieved"], "unit": e["unit"], "frac": e["frac"]}
     name, calls, tot_ms, flops, nb = max(stages, key=lambda x: x[2])
     roof = _roof_entry_by_intensity(name, calls, tot_ms, flops, nb)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic("decode", name)
     roof["launches_per_step"] = calls // prof_steps
     out = {"metric": "decode tokens/sec (KV-cached forward + top-k sampling) on 1 MI355X",
            "value": round(batch / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
