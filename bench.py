@@ -378,16 +378,26 @@ def bench_tables(a, B):
     y_v = torch.zeros(N, D, device="cuda", dtype=torch.bfloat16)
     h_x0 = torch.empty(N, device="cuda", dtype=torch.int32)
     h_v = torch.empty(N, device="cuda", dtype=torch.int32)
-    ws = torch.empty(max(B.bigram_workspace_bytes(N, D, tc.x0_rows),
-                         B.bigram_workspace_bytes(N, D, tc.v_rows)), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(B.bigram_workspace_bytes(N, D, tc.x0_rows), dtype=torch.uint8, device="cuda")
+    ws_v = torch.empty(B.bigram_workspace_bytes(N, D, tc.v_rows), dtype=torch.uint8, device="cuda")
     parts = [("gather_x0", lambda: B.bigram_fwd(tok, 2, tc.vocab, tx0, y_x0, h_x0)),
              ("gather_v", lambda: B.bigram_fwd(tok, 2, tc.vocab, tv, y_v, h_v)),
              ("update_x0", lambda: B.bigram_bwd_update(h_x0, dy, tx0, v_x0, tc.lr, tc.beta2, tc.eps, ws)),
-             ("update_v", lambda: B.bigram_bwd_update(h_v, dy, tv, v_v, tc.lr, tc.beta2, tc.eps, ws))]
+             ("update_v", lambda: B.bigram_bwd_update(h_v, dy, tv, v_v, tc.lr, tc.beta2, tc.eps, ws_v))]
+    # the two tables are independent: the value table's gather and update run on a second
+    # stream (default priority, its own workspace), joined at the end of the step, so the short
+    # launches of the two updates (sort passes, edge finish) overlap
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
 
     def step():
-        for _, fn in parts:
-            fn()
+        side.wait_stream(main)
+        parts[0][1]()
+        with torch.cuda.stream(side):
+            parts[1][1]()
+        parts[2][1]()
+        with torch.cuda.stream(side):
+            parts[3][1]()
+        main.wait_stream(side)
 
     ms, wall = time_steps(step, a.steps, a.warmup)
     # per-part event timing over the same number of steps
