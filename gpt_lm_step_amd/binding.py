@@ -25,7 +25,8 @@ EXPORTS = [
     "gpt_last_error", "gpt_status_string", "gpt_opt_state_elems", "gpt_opt_workspace_bytes",
     "gpt_opt_step", "gpt_lr_multiplier", "gpt_muon_momentum", "gpt_infer_workspace_bytes",
     "gpt_infer_init", "gpt_infer_reset", "gpt_infer_position", "gpt_infer_forward",
-    "gpt_infer_profile", "gpt_infer_profile_read", "gpt_infer_destroy", "gpt_sample",
+    "gpt_infer_profile", "gpt_infer_profile_read", "gpt_infer_check_errors", "gpt_infer_destroy",
+    "gpt_sample",
 ]
 # Every symbol include/gpt_kernels.h declares.
 KERNEL_EXPORTS = [
@@ -115,6 +116,7 @@ def lib() -> C.CDLL:
             "gpt_infer_forward": (i32, [vp, vp, vp, i32, i32, vp, vp]),
             "gpt_infer_profile": (i32, [vp, i32]),
             "gpt_infer_profile_read": (i32, [vp, vp, C.POINTER(i32)]),
+            "gpt_infer_check_errors": (i32, [vp, vp, C.POINTER(i32)]),
             "gpt_infer_destroy": (i32, [vp]),
             "gpt_sample": (i32, [vp, i32, i32, f32, i32, vp, vp, vp]),
         }
@@ -432,6 +434,12 @@ def gpt_infer_profile_read(ctx: InferContext):
     _check(lib().gpt_infer_profile_read(ctx.handle, arr, C.byref(n)))
     return [(arr[i].name.decode(), arr[i].calls, arr[i].ms, arr[i].flops, arr[i].bytes)
             for i in range(min(n.value, 256))]
+
+
+def gpt_infer_check_errors(ctx: InferContext, stream=None) -> int:
+    f = C.c_int32(0)
+    _check(lib().gpt_infer_check_errors(ctx.handle, _stream(stream), C.byref(f)))
+    return f.value
 
 
 def gpt_infer_destroy(ctx: InferContext):

@@ -821,6 +821,7 @@ gpt_status gpt_infer_init(const gpt_config* cfg, int32_t max_batch, int32_t max_
     st = launch_rope_table<float>((float*)c->cos_t, (float*)c->sin_t, max_seq, cfg->head_dim,
                                   cfg->rope_base, stream);
   }
+  if (st == GPT_OK) st = launch_fill((float*)c->err, 1, 0.f, stream);  // no problems seen yet
   if (st != GPT_OK) {
     delete c;
     return st;
@@ -866,6 +867,16 @@ gpt_status gpt_sample(const float* logits, int32_t B, int32_t V, float temperatu
   else
     sample_kernel<64><<<B, SAMPLE_THREADS, 0, stream>>>(logits, V, temperature, top_k, uniforms, tokens);
   return check_launch("sample");
+}
+
+gpt_status gpt_infer_check_errors(gpt_infer* ctx, hipStream_t stream, int32_t* flags) {
+  if (!ctx || !flags) return fail(GPT_EINVAL, "gpt_infer_check_errors: null argument");
+  int32_t h = 0;
+  if (hipMemcpyAsync(&h, ctx->err, sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return fail(GPT_EHIP, "gpt_infer_check_errors: copy failed");
+  *flags = h;
+  return launch_fill((float*)ctx->err, 1, 0.f, stream);
 }
 
 gpt_status gpt_infer_profile(gpt_infer* ctx, int32_t enable) {

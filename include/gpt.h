@@ -208,7 +208,8 @@ double gpt_muon_momentum(int64_t it);
  * the softcapped logits of each sequence's last position, fp32 [B, V], and advances the position.
  * Arguments (device pointers unless stated): params = the flat parameter buffer of
  * gpt_param_layout in cfg->dtype, 16-byte aligned; tokens = int32 [B, T] row-major (ids outside
- * [0, vocab) are clamped into it, as in gpt_fwd_bwd); logits = fp32 [B, V], 16-byte aligned.
+ * [0, vocab) are clamped into it and reported by gpt_infer_check_errors, as in gpt_fwd_bwd);
+ * logits = fp32 [B, V], 16-byte aligned.
  * The workspace (device, 256-byte aligned, gpt_infer_workspace_bytes) belongs to the caller and
  * must outlive the context; the context itself is host memory released by gpt_infer_destroy.
  * Work is queued on `stream` (results valid once it has run); init queues the rotary tables on
@@ -236,6 +237,9 @@ gpt_status gpt_infer_forward(gpt_infer* ctx, const void* params, const int32_t* 
  * entries [host]. */
 gpt_status gpt_infer_profile(gpt_infer* ctx, int32_t enable);
 gpt_status gpt_infer_profile_read(gpt_infer* ctx, gpt_profile_entry* out, int32_t* count);
+/* Bit flags of problems the context's kernels detected since init or the last call (1 = an input
+ * id outside [0, vocab)); synchronises `stream`, then clears the flags.  flags [host]. */
+gpt_status gpt_infer_check_errors(gpt_infer* ctx, hipStream_t stream, int32_t* flags);
 gpt_status gpt_infer_destroy(gpt_infer* ctx);
 /* Next-token choice per row of logits [B, V] fp32 (GPT.generate): temperature 0 -> argmax (the
  * first of equal maxima); otherwise logits below the top_k-th largest are dropped (top_k 0 or

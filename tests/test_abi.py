@@ -197,6 +197,7 @@ def test_inference_argument_checks_without_gpu():
     assert L.gpt_infer_reset(None) == B.GPT_EINVAL
     assert L.gpt_infer_forward(None, 256, 256, 1, 1, 256, None) == B.GPT_EINVAL
     assert L.gpt_infer_profile(None, 1) == B.GPT_EINVAL
+    assert L.gpt_infer_check_errors(None, None, C.byref(C.c_int32(0))) == B.GPT_EINVAL
     assert L.gpt_infer_profile_read(None, None, C.byref(C.c_int32(0))) == B.GPT_EINVAL
     assert L.gpt_sample(None, 0, 10, 1.0, 0, None, None, None) == B.GPT_OK          # empty batch
     assert L.gpt_sample(256, 1, 0, 1.0, 0, 256, 256, None) == B.GPT_ESHAPE

@@ -93,6 +93,25 @@ def test_next_logits_after_a_single_token():
     _check_logits(got, oi.next_logits(cfg, params, tok), False)
 
 
+def test_out_of_range_ids_are_clamped_and_reported():
+    """An id >= vocab (or < 0) is read as the nearest valid id, flagged, and the flag clears on
+    reading; the logits equal those of the clamped ids."""
+    cfg = configs.TINY
+    params, flat = _model(cfg, 205)
+    ctx = B.gpt_infer_init(cfg, 2, 8)
+    assert B.gpt_infer_check_errors(ctx) == 0
+    tok = inputs.uniform_tokens(13, (2, 4), cfg.vocab)
+    bad = tok.copy()
+    bad[0, 1], bad[1, 3] = cfg.vocab + 5, -3
+    logits = torch.empty(2, cfg.vocab, device="cuda")
+    B.gpt_infer_forward(ctx, flat, dev(bad), logits)
+    assert B.gpt_infer_check_errors(ctx) == 1
+    assert B.gpt_infer_check_errors(ctx) == 0
+    clamped = np.clip(bad, 0, cfg.vocab - 1)
+    _check_logits(host(logits), oi.next_logits(cfg, params, clamped), False)
+    ctx.close()
+
+
 def test_reset_position_and_batch_rules():
     cfg = configs.TINY
     _, flat = _model(cfg, 203)
