@@ -532,13 +532,17 @@ def ns_groups(cfg):
     return g
 
 
-def ns_work(cfg, steps=5):
+def ns_work(cfg, steps=5, symmetric=True):
     """Newton-Schulz GEMM flops of one optimizer step and its launches (3 per step and batch):
-    X X^T (2 S^2 L), c A A + b A (2 S^3), B X + a X (2 R C S), S = min(R, C), L = max(R, C)."""
+    X X^T (2 S^2 L), c A A + b A (2 S^3), B X + a X (2 R C S), S = min(R, C), L = max(R, C).
+    The first two results are symmetric and only their upper-triangle tiles are computed: a share
+    (T + 1) / 2T of their flops for T = S / 256 tiles per side."""
     flops, launches = 0.0, 0
     for count, R, C in ns_groups(cfg):
         S, L = min(R, C), max(R, C)
-        flops += count * steps * (2.0 * S * S * L + 2.0 * S ** 3 + 2.0 * R * C * S)
+        T = -(-S // 256)
+        tri = (T + 1) / (2.0 * T) if symmetric else 1.0
+        flops += count * steps * (tri * (2.0 * S * S * L + 2.0 * S ** 3) + 2.0 * R * C * S)
         launches += 3 * steps
     return flops, launches
 
@@ -622,7 +626,7 @@ def cpu_baseline_opt(cfg):
         t0 = time.perf_counter()
         oo.muon_update(p, g, np.zeros_like(g), 0.02, 0.85, True, 5, bf16=True)
         dt = time.perf_counter() - t0
-    flops, _ = ns_work(cfg)
+    flops, _ = ns_work(cfg, symmetric=False)  # the oracle computes every product in full
     one = 5 * (2.0 * D ** 3 * 3)
     return {"value": round(dt * flops / one * 1e3, 1), "unit": "ms", "cores": cores, "kind": "oracle",
             "sample": f"one {D} x {D} Muon update with 5 bf16 Newton-Schulz steps (fp64 numpy), "

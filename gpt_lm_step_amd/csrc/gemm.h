@@ -137,24 +137,34 @@ struct EpiSplit {
 
 // out = res + acc (fp32 residual stream; out may equal res).
 // Batched bf16 products of the Newton-Schulz iteration (matrix z of a batch at out + z * bs):
-// a plain store, and out = alpha * acc + beta * add with `add` in the output's layout.
-struct EpiNsStore {
+// a plain store, and out = alpha * acc + beta * add with `add` in the output's layout.  With SYM
+// the product is known to be symmetric (X X^T, c A A + b A for symmetric A): the kernel computes
+// the upper-triangle tiles only and mirror() writes each off-diagonal tile's values transposed.
+template <bool SYM>
+struct EpiNsStoreT {
   bf16* out;
   long long ld, bs;
   using Pre = NoPre;
+  static constexpr bool symmetric = SYM;
   __device__ __forceinline__ void at_batch(int z) { out += (long long)z * bs; }
   __device__ __forceinline__ Pre load(int, int) const { return {}; }
   __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre&) const {
     store4(out + (long long)r * ld + c, v);
   }
+  __device__ __forceinline__ void mirror(int r, int c, const float (&v)[4], const Pre&) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[(long long)(c + i) * ld + r] = from_f32<bf16>(v[i]);
+  }
   GPT_EPI_CALL
 };
-struct EpiNsCombine {
+template <bool SYM>
+struct EpiNsCombineT {
   bf16* out;
   const bf16* add;
   long long ld, bs;
   float alpha, beta;
   using Pre = Pre4<bf16>;
+  static constexpr bool symmetric = SYM;
   __device__ __forceinline__ void at_batch(int z) {
     out += (long long)z * bs;
     add += (long long)z * bs;
@@ -162,14 +172,27 @@ struct EpiNsCombine {
   __device__ __forceinline__ Pre load(int r, int c) const {
     return pre_load(add + (long long)r * ld + c);
   }
-  __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre& a) const {
-    float o[4];
+  __device__ __forceinline__ void combine(const float (&v)[4], const Pre& a, float (&o)[4]) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = alpha * v[i] + beta * to_f32(a.x[i]);
+  }
+  __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre& a) const {
+    float o[4];
+    combine(v, a, o);
     store4(out + (long long)r * ld + c, o);
+  }
+  __device__ __forceinline__ void mirror(int r, int c, const float (&v)[4], const Pre& a) const {
+    float o[4];
+    combine(v, a, o);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[(long long)(c + i) * ld + r] = from_f32<bf16>(o[i]);
   }
   GPT_EPI_CALL
 };
+using EpiNsStore = EpiNsStoreT<false>;
+using EpiNsCombine = EpiNsCombineT<false>;
+using EpiNsStoreSym = EpiNsStoreT<true>;
+using EpiNsCombineSym = EpiNsCombineT<true>;
 
 struct EpiResid {
   const float* res;
@@ -279,6 +302,12 @@ enum GemmSite {
   G_INF_DOWN, G_INF_HEAD
 };
 
+// Epilogues of products known to be symmetric (see EpiNsStoreT).
+template <class E, class = void>
+struct is_symmetric : std::false_type {};
+template <class E>
+struct is_symmetric<E, std::enable_if_t<E::symmetric>> : std::true_type {};
+
 namespace gemm_detail {
 
 constexpr int THREADS = 256;  // 4 waves in a 2 x 2 grid; each wave owns a (BM/2) x (BN/2) tile
@@ -386,6 +415,18 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   const int in = L % per_group;
   tm = first_m + in % gm;
   tn = in / gm;
+}
+
+// Upper-triangle tiles of a T x T tile grid (symmetric products): block b -> the b-th tile
+// (tm <= tn) in row order.
+__device__ __forceinline__ void tri_coords(int T, int& tm, int& tn) {
+  int L = blockIdx.x, r = 0;
+  while (L >= T - r) {
+    L -= T - r;
+    ++r;
+  }
+  tm = r;
+  tn = r + L;
 }
 
 // BM x BN output tile per workgroup; each wave computes (BM/2) x (BN/2) as (BM/64) x (BN/64)
@@ -634,7 +675,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
   static_assert(NS >= 2 && (NS - 2) * PER_TILE < 64, "pipeline depth");
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  if constexpr (is_symmetric<Epi>::value) tri_coords(tiles_m, tm, tn);
+  else tile_coords(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE;
   const int wm = (w / WGN) * WTM, wn = (w % WGN) * WTN;
@@ -797,6 +839,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
         if (row < M && col < N) {
           const float v[4] = {x[0], x[1], x[2], x[3]};
           epi.store(row, col, v, pre[p]);
+          if constexpr (is_symmetric<Epi>::value)
+            if (tm != tn) epi.mirror(row, col, v, pre[p]);
         }
       }
     }
@@ -841,7 +885,9 @@ void launch_dma(bool a_kc, bool b_kc, int M, int N, int K, const bf16* A, long l
                 const bf16* B, long long ldb, const Epi& epi, hipStream_t s, int splits = 1,
                 int batch = 1, long long a_bs = 0, long long b_bs = 0) {
   const int kps = splits > 1 ? (int)cdiv(cdiv(K, splits), 64) * 64 : K;  // K per split
-  dim3 grid((unsigned)(cdiv(M, BM) * cdiv(N, BN)), (unsigned)cdiv(K, kps), (unsigned)batch);
+  const long long T = cdiv(M, BM);  // symmetric products: the upper triangle of a T x T grid
+  const long long tiles = is_symmetric<Epi>::value ? T * (T + 1) / 2 : (long long)cdiv(M, BM) * cdiv(N, BN);
+  dim3 grid((unsigned)tiles, (unsigned)cdiv(K, kps), (unsigned)batch);
   // each split's operand spans at most these bytes from its own start
   const uint32_t ab = (uint32_t)operand_bytes(a_kc, M, kps, lda, 2);
   const uint32_t bb = (uint32_t)operand_bytes(b_kc, N, kps, ldb, 2);
@@ -921,6 +967,7 @@ inline gpt_status gemm_batched(bool a_kc, bool b_kc, int M, int N, int K, const 
                                long long b_bs, int batch, const Epi& epi, hipStream_t s) {
   static_assert(gemm_detail::has_batch<Epi>::value, "batched launches need an at_batch epilogue");
   if (batch <= 0 || M <= 0 || N <= 0) return GPT_OK;
+  if (is_symmetric<Epi>::value && M != N) return fail(GPT_ESHAPE, "gemm_batched: a symmetric product is square");
   if (batch > 65535) return fail(GPT_ESHAPE, "gemm_batched: at most 65535 matrices");
   if (K <= 0 || K % 8) return fail(GPT_ESHAPE, "gemm: K must be a positive multiple of 8");
   if (lda % 8 || ldb % 8 || a_bs % 8 || b_bs % 8)

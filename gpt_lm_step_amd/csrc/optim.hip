@@ -267,13 +267,13 @@ gpt_status ns_iterate(const MatGroup& G, const OptWs& w, int steps, bf16** resul
     gpt_status st;
     if (!tall)
       st = gemm_batched<G_NS_GRAM>(true, true, S, S, C, x, C, xn, x, C, xn, Z,
-                                   EpiNsStore{w.a, S, sn}, s);
+                                   EpiNsStoreSym{w.a, S, sn}, s);
     else
       st = gemm_batched<G_NS_GRAM>(false, false, S, S, R, x, C, xn, x, C, xn, Z,
-                                   EpiNsStore{w.a, S, sn}, s);
+                                   EpiNsStoreSym{w.a, S, sn}, s);
     if (st != GPT_OK) return st;
     st = gemm_batched<G_NS_POLY>(true, true, S, S, S, w.a, S, sn, w.a, S, sn, Z,
-                                 EpiNsCombine{w.b, w.a, S, sn, NS_C, NS_B}, s);
+                                 EpiNsCombineSym{w.b, w.a, S, sn, NS_C, NS_B}, s);
     if (st != GPT_OK) return st;
     if (!tall)
       st = gemm_batched<G_NS_APPLY>(true, false, R, C, R, w.b, S, sn, x, C, xn, Z,
