@@ -139,7 +139,8 @@ struct EpiSplit {
 // Batched bf16 products of the Newton-Schulz iteration (matrix z of a batch at out + z * bs):
 // a plain store, and out = alpha * acc + beta * add with `add` in the output's layout.  With SYM
 // the product is known to be symmetric (X X^T, c A A + b A for symmetric A): the kernel computes
-// the upper-triangle tiles only and mirror() writes each off-diagonal tile's values transposed.
+// the upper-triangle tiles only and mirror_col() writes each off-diagonal tile's values
+// transposed, one mirrored row run of 32 per lane read back from the staged tile.
 template <bool SYM>
 struct EpiNsStoreT {
   bf16* out;
@@ -151,9 +152,15 @@ struct EpiNsStoreT {
   __device__ __forceinline__ void store(int r, int c, const float (&v)[4], const Pre&) const {
     store4(out + (long long)r * ld + c, v);
   }
-  __device__ __forceinline__ void mirror(int r, int c, const float (&v)[4], const Pre&) const {
+  // the mirrored run: out[c][r0 .. r0+31] = v[0 .. 31] (v = column c of rows r0..r0+31)
+  __device__ __forceinline__ void mirror_col(int r0, int c, const float (&v)[32]) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[(long long)(c + i) * ld + r] = from_f32<bf16>(v[i]);
+    for (int q = 0; q < 4; ++q) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = v[q * 8 + e];
+      store8_f32(out + (long long)c * ld + r0 + q * 8, o);
+    }
   }
   GPT_EPI_CALL
 };
@@ -181,11 +188,17 @@ struct EpiNsCombineT {
     combine(v, a, o);
     store4(out + (long long)r * ld + c, o);
   }
-  __device__ __forceinline__ void mirror(int r, int c, const float (&v)[4], const Pre& a) const {
-    float o[4];
-    combine(v, a, o);
+  // the mirrored run: out[c][r0 .. r0+31] = alpha v + beta add[c][r0 ..] (add is symmetric, so
+  // its mirrored entries equal the ones the direct store used)
+  __device__ __forceinline__ void mirror_col(int r0, int c, const float (&v)[32]) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[(long long)(c + i) * ld + r] = from_f32<bf16>(o[i]);
+    for (int q = 0; q < 4; ++q) {
+      float a8[8], o[8];
+      load8_f32(add + (long long)c * ld + r0 + q * 8, a8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = alpha * v[q * 8 + e] + beta * a8[e];
+      store8_f32(out + (long long)c * ld + r0 + q * 8, o);
+    }
   }
   GPT_EPI_CALL
 };
@@ -839,8 +852,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
         if (row < M && col < N) {
           const float v[4] = {x[0], x[1], x[2], x[3]};
           epi.store(row, col, v, pre[p]);
-          if constexpr (is_symmetric<Epi>::value)
-            if (tm != tn) epi.mirror(row, col, v, pre[p]);
+        }
+      }
+      if constexpr (is_symmetric<Epi>::value) {
+        // off-diagonal tiles of a symmetric product: lane c reads column c of the staged 32-row
+        // slice and writes it as the run out[n0 + wn + c][m0 + wm + i*32 ..] (tile-aligned sizes)
+        static_assert(WTN == WAVE, "the column read-back gives each lane one column");
+        if (tm != tn) {
+          const int c = lane, r0 = m0 + wm + i * 32;
+          float cv[32];
+#pragma unroll
+          for (int r = 0; r < 32; ++r) cv[r] = ep[r * WTN + (((c / 4) ^ (r % 16)) * 4) + c % 4];
+          epi.mirror_col(r0, n0 + wn + c, cv);
         }
       }
     }
@@ -967,7 +990,8 @@ inline gpt_status gemm_batched(bool a_kc, bool b_kc, int M, int N, int K, const 
                                long long b_bs, int batch, const Epi& epi, hipStream_t s) {
   static_assert(gemm_detail::has_batch<Epi>::value, "batched launches need an at_batch epilogue");
   if (batch <= 0 || M <= 0 || N <= 0) return GPT_OK;
-  if (is_symmetric<Epi>::value && M != N) return fail(GPT_ESHAPE, "gemm_batched: a symmetric product is square");
+  if (is_symmetric<Epi>::value && (M != N || M % 256))
+    return fail(GPT_ESHAPE, "gemm_batched: a symmetric product is square with a multiple of 256 rows");
   if (batch > 65535) return fail(GPT_ESHAPE, "gemm_batched: at most 65535 matrices");
   if (K <= 0 || K % 8) return fail(GPT_ESHAPE, "gemm: K must be a positive multiple of 8");
   if (lda % 8 || ldb % 8 || a_bs % 8 || b_bs % 8)

@@ -263,17 +263,20 @@ gpt_status ns_iterate(const MatGroup& G, const OptWs& w, int steps, bf16** resul
   const int S = tall ? C : R;
   const long long xn = (long long)R * C, sn = (long long)S * S;
   bf16 *x = w.x0, *xn_ = w.x1;
+  // the two symmetric products compute their upper-triangle tiles only when S is tile-aligned
+  const bool sym = S % 256 == 0;
+  auto gram = [&](auto epi) {
+    return !tall ? gemm_batched<G_NS_GRAM>(true, true, S, S, C, x, C, xn, x, C, xn, Z, epi, s)
+                 : gemm_batched<G_NS_GRAM>(false, false, S, S, R, x, C, xn, x, C, xn, Z, epi, s);
+  };
+  auto poly = [&](auto epi) {
+    return gemm_batched<G_NS_POLY>(true, true, S, S, S, w.a, S, sn, w.a, S, sn, Z, epi, s);
+  };
   for (int it = 0; it < steps; ++it) {
-    gpt_status st;
-    if (!tall)
-      st = gemm_batched<G_NS_GRAM>(true, true, S, S, C, x, C, xn, x, C, xn, Z,
-                                   EpiNsStoreSym{w.a, S, sn}, s);
-    else
-      st = gemm_batched<G_NS_GRAM>(false, false, S, S, R, x, C, xn, x, C, xn, Z,
-                                   EpiNsStoreSym{w.a, S, sn}, s);
+    gpt_status st = sym ? gram(EpiNsStoreSym{w.a, S, sn}) : gram(EpiNsStore{w.a, S, sn});
     if (st != GPT_OK) return st;
-    st = gemm_batched<G_NS_POLY>(true, true, S, S, S, w.a, S, sn, w.a, S, sn, Z,
-                                 EpiNsCombineSym{w.b, w.a, S, sn, NS_C, NS_B}, s);
+    st = sym ? poly(EpiNsCombineSym{w.b, w.a, S, sn, NS_C, NS_B})
+             : poly(EpiNsCombine{w.b, w.a, S, sn, NS_C, NS_B});
     if (st != GPT_OK) return st;
     if (!tall)
       st = gemm_batched<G_NS_APPLY>(true, false, R, C, R, w.b, S, sn, x, C, xn, Z,
