@@ -330,8 +330,22 @@ __global__ __launch_bounds__(64 * NWV, NWV == 8 ? 1 : 2) void attn_fwd_kernel(
           mx = fmaxf(mx, sc[st2][r]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-      const float mn = fmaxf(m, mx);
-      const float nb = -mn * sl2;
+      // The reference max m may lag the true running max: weights are 2^(sl2 (s - m)), so O, l
+      // and the saved LSE2 = sl2 m + log2 l all refer to the same m and the result is exact
+      // whatever m is, as long as the weights stay in range.  m is raised (and O, l rescaled)
+      // only when some row's scores exceed it by more than 2^8 in weight, which after the first
+      // tile is rare, instead of on every tile where some row's max moves.
+      if (!__all((mx - m) * sl2 <= 8.f)) {  // also taken on the first tile (m = -inf)
+        const float mn = fmaxf(m, mx);
+        const float alpha = fast_exp2((m - mn) * sl2);  // 0 on the first tile, 1 where unchanged
+#pragma unroll
+        for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        l *= alpha;
+        m = mn;
+      }
+      const float nb = -m * sl2;
       float sum = 0.f;
 #pragma unroll
       for (int st2 = 0; st2 < 2; ++st2)
@@ -342,17 +356,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 8 ? 1 : 2) void attn_fwd_kernel(
           sum += pv;
         }
       sum += __shfl_xor(sum, 32, WAVE);
-      // rescale the running output only when some row's max moved (rare after the first tiles)
-      if (!__all(mn == m)) {
-        const float alpha = fast_exp2((m - mn) * sl2);
-#pragma unroll
-        for (int dt = 0; dt < HD / 32; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-        l *= alpha;
-      }
       l += sum;
-      m = mn;
 #pragma unroll
       for (int st2 = 0; st2 < 2; ++st2)
 #pragma unroll
