@@ -378,8 +378,8 @@ def bench_tables(a, B):
     y_v = torch.zeros(N, D, device="cuda", dtype=torch.bfloat16)
     h_x0 = torch.empty(N, device="cuda", dtype=torch.int32)
     h_v = torch.empty(N, device="cuda", dtype=torch.int32)
-    ws = torch.empty(B.bigram_workspace_bytes(N, D, tc.x0_rows), dtype=torch.uint8, device="cuda")
-    ws_v = torch.empty(B.bigram_workspace_bytes(N, D, tc.v_rows), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(B.bigram_workspace_bytes(N, D), dtype=torch.uint8, device="cuda")
+    ws_v = torch.empty(B.bigram_workspace_bytes(N, D), dtype=torch.uint8, device="cuda")
     parts = [("gather_x0", lambda: B.bigram_fwd(tok, 2, tc.vocab, tx0, y_x0, h_x0)),
              ("gather_v", lambda: B.bigram_fwd(tok, 2, tc.vocab, tv, y_v, h_v)),
              ("update_x0", lambda: B.bigram_bwd_update(h_x0, dy, tx0, v_x0, tc.lr, tc.beta2, tc.eps, ws)),
@@ -469,8 +469,7 @@ def bench_speedrun(a, B):
     d_v = torch.empty(MB * N, D, device="cuda", dtype=bf)
     h_x0 = torch.empty(MB * N, device="cuda", dtype=torch.int32)
     h_v = torch.empty(MB * N, device="cuda", dtype=torch.int32)
-    ws = torch.empty(max(B.bigram_workspace_bytes(MB * N, D, tc.x0_rows),
-                         B.bigram_workspace_bytes(MB * N, D, tc.v_rows)), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(B.bigram_workspace_bytes(MB * N, D), dtype=torch.uint8, device="cuda")
 
     def step():
         for i in range(MB):

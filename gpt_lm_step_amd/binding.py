@@ -46,7 +46,8 @@ class gpt_config(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("n_layer", "d_model", "n_head", "n_kv_head", "head_dim",
                                          "d_mlp", "vocab", "seq_len", "batch", "dtype")] + \
                [("rms_eps", C.c_float), ("rope_base", C.c_float), ("softcap", C.c_float)] + \
-               [(n, C.c_int32) for n in ("qk_norm", "has_x0_add", "has_v_add", "has_trigram")]
+               [(n, C.c_int32) for n in ("qk_norm", "has_x0_add", "has_v_add", "has_trigram",
+                                         "ce_chunk_tokens")]
 
 
 class gpt_profile_entry(C.Structure):
@@ -86,7 +87,7 @@ def lib() -> C.CDLL:
             "gpt_profile": (i32, [vp, i32]),
             "gpt_profile_read": (i32, [vp, vp, C.POINTER(i32)]),
             "bigram_fwd": (i32, [vp, i32, i32, i32, i32, vp, i64, i32, i32, vp, vp, vp]),
-            "bigram_workspace_bytes": (sz, [i64, i32, i64]),
+            "bigram_workspace_bytes": (sz, [i64, i32]),
             "bigram_bwd_update": (i32, [vp, vp, i64, i32, i32, vp, vp, i64, f32, f32, f32, vp,
                                         sz, vp]),
             "gpt_last_error": (C.c_char_p, []),
@@ -146,7 +147,7 @@ def make_config(cfg: GPTConfig) -> gpt_config:
     return gpt_config(cfg.n_layer, cfg.d_model, cfg.n_head, cfg.n_kv_head, cfg.head_dim,
                       cfg.d_mlp, cfg.vocab, cfg.seq_len, cfg.batch, cfg.dtype, cfg.rms_eps,
                       cfg.rope_base, cfg.softcap, cfg.qk_norm, cfg.has_x0_add, cfg.has_v_add,
-                      cfg.has_trigram)
+                      cfg.has_trigram, cfg.ce_chunk_tokens)
 
 
 def gpt_param_layout(cfg: GPTConfig) -> Tuple[List[Tuple[str, int, Tuple[int, int]]], int]:
@@ -246,15 +247,15 @@ def bigram_fwd(tokens, order: int, vocab: int, table, y, h_out=None, stream=None
                             _stream(stream)))
 
 
-def bigram_workspace_bytes(n: int, dim: int, rows: int) -> int:
-    return int(lib().bigram_workspace_bytes(n, dim, rows))
+def bigram_workspace_bytes(n: int, dim: int) -> int:
+    return int(lib().bigram_workspace_bytes(n, dim))
 
 
 def bigram_bwd_update(h, dy, table, v, lr: float, beta2: float = 0.95, eps: float = 1e-8,
                       workspace=None, stream=None):
     import torch
     n, dim = dy.shape[0], dy.shape[1]
-    need = bigram_workspace_bytes(n, dim, table.shape[0])
+    need = bigram_workspace_bytes(n, dim)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dy.device)
     _check(lib().bigram_bwd_update(_ptr(h), _ptr(dy), n, dim, _dtype_code(table), _ptr(table),

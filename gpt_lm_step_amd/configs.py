@@ -40,6 +40,7 @@ class GPTConfig:
     has_x0_add: int = 0
     has_v_add: int = 0
     has_trigram: int = 0
+    ce_chunk_tokens: int = 0     # LM-head / cross-entropy chunk (0: library default)
     name: str = ""
 
     @property

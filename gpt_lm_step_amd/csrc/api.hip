@@ -74,7 +74,7 @@ const char* gpt_status_string(gpt_status s) {
 }
 
 gpt_status bigram_fwd(const int32_t* tokens, int32_t B, int32_t T, int32_t order, int32_t vocab,
-                      const void* table, int64_t rows, int32_t dim, int32_t dtype, void* y,
+                      const void* table, int64_t rows, int32_t dim, gpt_dtype dtype, void* y,
                       int32_t* h_out, hipStream_t stream) {
   if (B < 0 || T < 0) return fail(GPT_ESHAPE, "bigram_fwd: negative B or T");
   if ((long long)B * T == 0) return GPT_OK;
@@ -92,14 +92,13 @@ gpt_status bigram_fwd(const int32_t* tokens, int32_t B, int32_t T, int32_t order
   return fail(GPT_EINVAL, "bigram_fwd: bad dtype");
 }
 
-size_t bigram_workspace_bytes(int64_t n, int32_t dim, int64_t rows) {
-  (void)rows;
+size_t bigram_workspace_bytes(int64_t n, int32_t dim) {
   if (n <= 0 || dim <= 0) return 0;
   return segsum_workspace_bytes(n, dim);
 }
 
 gpt_status bigram_bwd_update(const int32_t* h, const void* dy, int64_t n, int32_t dim,
-                             int32_t dtype, void* table, float* v, int64_t rows, float lr,
+                             gpt_dtype dtype, void* table, float* v, int64_t rows, float lr,
                              float beta2, float eps, void* workspace, size_t ws_bytes,
                              hipStream_t stream) {
   if (n < 0 || n >= (1LL << 31)) return fail(GPT_ESHAPE, "bigram_bwd_update: n out of range");
@@ -108,7 +107,7 @@ gpt_status bigram_bwd_update(const int32_t* h, const void* dy, int64_t n, int32_
   if (dim <= 0 || dim % 8 || dim > 2048)
     return fail(GPT_ESHAPE, "bigram_bwd_update: dim must be a multiple of 8 in [8, 2048]");
   if (rows < 1 || rows >= (1LL << 31)) return fail(GPT_ERANGE, "bigram_bwd_update: rows out of range");
-  if (!workspace || ws_bytes < bigram_workspace_bytes(n, dim, rows))
+  if (!workspace || ws_bytes < bigram_workspace_bytes(n, dim))
     return fail(GPT_EWORKSPACE, "bigram_bwd_update: workspace too small");
   if (((uintptr_t)workspace) % 256) return fail(GPT_EINVAL, "bigram_bwd_update: workspace not 256-byte aligned");
   if (dtype == GPT_BF16)

@@ -11,7 +11,7 @@ bool bad_dtype(int32_t d) { return d != GPT_F32 && d != GPT_BF16; }
 
 extern "C" {
 
-gpt_status gptk_gemm(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32_t N, int32_t K,
+gpt_status gptk_gemm(gpt_dtype dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32_t N, int32_t K,
                      const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
                      int64_t ldc, int32_t beta, hipStream_t stream) {
   if (bad_dtype(dtype) || !A || !B || !C) return fail(GPT_EINVAL, "gptk_gemm: bad dtype or null");
@@ -23,7 +23,7 @@ gpt_status gptk_gemm(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32
   return gemm<G_TEST, float>(a_kc, b_kc, M, N, K, (const float*)A, lda, (const float*)B, ldb, epi, stream);
 }
 
-gpt_status gptk_gemm_wgrad(int32_t dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32_t N,
+gpt_status gptk_gemm_wgrad(gpt_dtype dtype, int32_t a_kc, int32_t b_kc, int32_t M, int32_t N,
                            int32_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
                            float* C, int64_t ldc, int32_t beta, float* ws, int64_t ws_floats,
                            hipStream_t stream) {
@@ -44,7 +44,7 @@ int64_t gptk_gemm_wgrad_ws_floats(int32_t M, int32_t N, int32_t K) {
   return gemm_wgrad_ws_floats(M, N, K);
 }
 
-gpt_status gptk_rmsnorm_fwd(int32_t dtype, const float* x, void* y, float* rstd, int64_t N,
+gpt_status gptk_rmsnorm_fwd(gpt_dtype dtype, const float* x, void* y, float* rstd, int64_t N,
                             int32_t D, float eps, hipStream_t stream) {
   if (bad_dtype(dtype) || !x || !y || !rstd) return fail(GPT_EINVAL, "gptk_rmsnorm_fwd: null");
   if (N < 0 || D <= 0 || D % 64 || D > 2048) return fail(GPT_ESHAPE, "gptk_rmsnorm_fwd: bad D");
@@ -53,7 +53,7 @@ gpt_status gptk_rmsnorm_fwd(int32_t dtype, const float* x, void* y, float* rstd,
   return launch_rms_fwd<float>(x, (float*)y, rstd, N, D, eps, stream);
 }
 
-gpt_status gptk_rmsnorm_bwd(int32_t dtype, const float* x, const float* rstd, const float* dy,
+gpt_status gptk_rmsnorm_bwd(gpt_dtype dtype, const float* x, const float* rstd, const float* dy,
                             const float* dres, float* dx, void* dx_t, int64_t N, int32_t D,
                             hipStream_t stream) {
   if (bad_dtype(dtype) || !x || !rstd || !dy || !dx) return fail(GPT_EINVAL, "gptk_rmsnorm_bwd: null");
@@ -64,7 +64,7 @@ gpt_status gptk_rmsnorm_bwd(int32_t dtype, const float* x, const float* rstd, co
   return launch_rms_bwd<float>(x, rstd, dy, dres, dx, (float*)dx_t, N, D, stream);
 }
 
-gpt_status gptk_rope_table(int32_t dtype, void* cos_t, void* sin_t, int32_t T, int32_t hd,
+gpt_status gptk_rope_table(gpt_dtype dtype, void* cos_t, void* sin_t, int32_t T, int32_t hd,
                            float base, hipStream_t stream) {
   if (bad_dtype(dtype) || !cos_t || !sin_t) return fail(GPT_EINVAL, "gptk_rope_table: null");
   if (T <= 0 || hd <= 0 || hd % 2) return fail(GPT_ESHAPE, "gptk_rope_table: bad sizes");
@@ -78,7 +78,7 @@ static gpt_status check_heads(int64_t N, int32_t T, int32_t H, int32_t hd) {
   return GPT_OK;
 }
 
-gpt_status gptk_rope_qknorm_fwd(int32_t dtype, void* qkv, const void* cos_t, const void* sin_t,
+gpt_status gptk_rope_qknorm_fwd(gpt_dtype dtype, void* qkv, const void* cos_t, const void* sin_t,
                                 float* rstd_qk, int64_t N, int32_t T, int32_t H, int32_t hd,
                                 int32_t qk_norm, float eps, hipStream_t stream) {
   if (bad_dtype(dtype) || !qkv || !cos_t || !sin_t || !rstd_qk) return fail(GPT_EINVAL, "gptk_rope_qknorm_fwd: null");
@@ -91,7 +91,7 @@ gpt_status gptk_rope_qknorm_fwd(int32_t dtype, void* qkv, const void* cos_t, con
                                        rstd_qk, N, T, H, hd, qk_norm, eps, stream);
 }
 
-gpt_status gptk_rope_qknorm_bwd(int32_t dtype, void* dqkv, const void* qkv, const void* cos_t,
+gpt_status gptk_rope_qknorm_bwd(gpt_dtype dtype, void* dqkv, const void* qkv, const void* cos_t,
                                 const void* sin_t, const float* rstd_qk, int64_t N, int32_t T,
                                 int32_t H, int32_t hd, int32_t qk_norm, hipStream_t stream) {
   if (bad_dtype(dtype) || !dqkv || !qkv || !cos_t || !sin_t || !rstd_qk)
@@ -105,7 +105,7 @@ gpt_status gptk_rope_qknorm_bwd(int32_t dtype, void* dqkv, const void* qkv, cons
                                        (const float*)sin_t, rstd_qk, N, T, H, hd, qk_norm, stream);
 }
 
-gpt_status gptk_attention_fwd(int32_t dtype, const void* qkv, void* out, float* lse2, int32_t B,
+gpt_status gptk_attention_fwd(gpt_dtype dtype, const void* qkv, void* out, float* lse2, int32_t B,
                               int32_t T, int32_t H, int32_t hd, hipStream_t stream) {
   if (bad_dtype(dtype) || !qkv || !out || !lse2) return fail(GPT_EINVAL, "gptk_attention_fwd: null");
   if (B <= 0 || T <= 0 || T % 64) return fail(GPT_ESHAPE, "gptk_attention_fwd: T must be a multiple of 64");
@@ -116,7 +116,7 @@ gpt_status gptk_attention_fwd(int32_t dtype, const void* qkv, void* out, float* 
   return launch_attn_fwd<float>((const float*)qkv, (float*)out, lse2, B, T, H, hd, stream);
 }
 
-gpt_status gptk_attention_bwd(int32_t dtype, const void* qkv, const void* out, const void* dout,
+gpt_status gptk_attention_bwd(gpt_dtype dtype, const void* qkv, const void* out, const void* dout,
                               const float* lse2, float* scratch, void* dqkv, int32_t B,
                               int32_t T, int32_t H, int32_t hd, hipStream_t stream) {
   if (bad_dtype(dtype) || !qkv || !out || !dout || !lse2 || !scratch || !dqkv)
@@ -131,7 +131,7 @@ gpt_status gptk_attention_bwd(int32_t dtype, const void* qkv, const void* out, c
                                 scratch, (float*)dqkv, B, T, H, hd, stream);
 }
 
-gpt_status gptk_softcap_ce(int32_t dtype, void* z, int64_t ldz, const int32_t* targets,
+gpt_status gptk_softcap_ce(gpt_dtype dtype, void* z, int64_t ldz, const int32_t* targets,
                            int64_t rows, int32_t V, float cap, float grad_scale,
                            const int32_t* n_valid, float* loss_rows, hipStream_t stream) {
   if (bad_dtype(dtype) || !z || !targets || !n_valid || !loss_rows)

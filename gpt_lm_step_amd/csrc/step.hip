@@ -53,6 +53,8 @@ gpt_status validate(const gpt_config* c) {
   if ((long long)c->batch * c->seq_len >= (1LL << 31) / 8)
     return fail(GPT_ESHAPE, "too many tokens per step");
   if (c->dtype != GPT_F32 && c->dtype != GPT_BF16) return fail(GPT_EINVAL, "bad dtype");
+  if (c->ce_chunk_tokens < 0 || c->ce_chunk_tokens % 64)
+    return fail(GPT_ESHAPE, "ce_chunk_tokens must be 0 or a positive multiple of 64");
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f) || !(c->softcap >= 0.f))
     return fail(GPT_ERANGE, "rms_eps, rope_base or softcap out of range");
   return GPT_OK;
@@ -61,13 +63,15 @@ gpt_status validate(const gpt_config* c) {
 namespace {
 
 
-// Tokens of one head/cross-entropy chunk: all tokens when the bf16/fp32 logits fit in 2 GiB
-// (the most one GEMM operand may span).
+// Tokens of one head/cross-entropy chunk: the caller's choice, capped so that the bf16/fp32
+// logits chunk spans at most 2 GiB (the most one GEMM operand may span); by default all tokens
+// when they fit.
 long long ce_chunk_rows(const gpt_config& c) {
   const long long N = (long long)c.batch * c.seq_len;
   const long long esz = c.dtype == GPT_BF16 ? 2 : 4;
   long long rows = (2LL << 30) / ((long long)c.vocab * esz);
   rows = std::max<long long>(64, rows / 64 * 64);
+  if (c.ce_chunk_tokens > 0) rows = std::min<long long>(rows, c.ce_chunk_tokens);
   return std::min(N, rows);
 }
 

@@ -64,6 +64,12 @@ typedef struct {
   int32_t has_x0_add;  /* 1: a per-token addend is added to x0 (after the embedding norm) */
   int32_t has_v_add;   /* 1: a per-token addend is added to the values of every layer */
   int32_t has_trigram; /* 1: gathered trigram rows, projected by wtri [D,D], add to values */
+  int32_t ce_chunk_tokens; /* tokens per LM-head / cross-entropy chunk: 0 = as many as keep the
+                              logits chunk within 2 GiB (all tokens of every shipped workload);
+                              otherwise a multiple of 64.  Smaller chunks shrink the workspace
+                              (the logits chunk is [chunk, vocab] in dtype); the result does not
+                              depend on the chunking beyond fp32 summation order of the head's
+                              weight gradient. */
 } gpt_config;
 
 /* One entry of the flat parameter layout. */
@@ -259,11 +265,11 @@ gpt_status gpt_sample(const float* logits, int32_t B, int32_t V, float temperatu
  * tokens int32 [B,T]; table [rows, dim] and y [B*T, dim] in `dtype`; h_out int32 [B*T] or
  * NULL.  Requires dim % 8 == 0, 1 <= rows < 2^31, order in {2, 3}. */
 gpt_status bigram_fwd(const int32_t* tokens, int32_t B, int32_t T, int32_t order, int32_t vocab,
-                      const void* table, int64_t rows, int32_t dim, int32_t dtype, void* y,
+                      const void* table, int64_t rows, int32_t dim, gpt_dtype dtype, void* y,
                       int32_t* h_out, hipStream_t stream);
 
 /* Device workspace in bytes for bigram_bwd_update over n tokens of width dim [host]. */
-size_t bigram_workspace_bytes(int64_t n, int32_t dim, int64_t rows);
+size_t bigram_workspace_bytes(int64_t n, int32_t dim);
 
 /* Sparse table update inlined in the tables' backward (decoder-rtx: no first moment, one
  * magnitude per row, no .grad buffer).  For every row r hit by h (rows never hit are left
@@ -273,10 +279,10 @@ size_t bigram_workspace_bytes(int64_t n, int32_t dim, int64_t rows);
  *   table[r, :] -= lr * g_r / (sqrt(v[r]) + eps)   (uses the new v[r])
  * h int32 [n] (entries outside [0, rows) are skipped); dy [n, dim] in `dtype`; table
  * [rows, dim] in `dtype` and v fp32 [rows] updated in place.  workspace: at least
- * bigram_workspace_bytes(n, dim, rows) bytes, 256-byte aligned.  Requires dim % 8 == 0,
+ * bigram_workspace_bytes(n, dim) bytes, 256-byte aligned.  Requires dim % 8 == 0,
  * n < 2^31.  n == 0 is a no-op. */
 gpt_status bigram_bwd_update(const int32_t* h, const void* dy, int64_t n, int32_t dim,
-                             int32_t dtype, void* table, float* v, int64_t rows, float lr,
+                             gpt_dtype dtype, void* table, float* v, int64_t rows, float lr,
                              float beta2, float eps, void* workspace, size_t ws_bytes,
                              hipStream_t stream);
 

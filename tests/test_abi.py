@@ -56,6 +56,7 @@ def test_workspace_sizes_are_plausible():
     ("head_dim", 48, B.GPT_ESHAPE), ("n_kv_head", 2, B.GPT_ESHAPE), ("vocab", 500, B.GPT_ESHAPE),
     ("seq_len", 100, B.GPT_ESHAPE), ("dtype", 7, B.GPT_EINVAL), ("n_layer", 0, B.GPT_ESHAPE),
     ("vocab", 65536 + 64, B.GPT_ESHAPE), ("d_model", 4096, B.GPT_ESHAPE),
+    ("ce_chunk_tokens", 100, B.GPT_ESHAPE), ("ce_chunk_tokens", -64, B.GPT_ESHAPE),
 ])
 def test_invalid_configs_are_rejected(field, value, status):
     c = B.make_config(configs.TINY)
@@ -66,6 +67,19 @@ def test_invalid_configs_are_rejected(field, value, status):
     b = C.c_size_t(0)
     assert B.lib().gpt_workspace_bytes(C.byref(c), C.byref(b)) == status
     assert len(B.lib().gpt_last_error()) > 0
+
+
+def test_cross_entropy_chunk_shrinks_the_workspace_by_its_logits():
+    """A chunk of C tokens keeps a [C, vocab] logits buffer instead of [N, vocab]; everything
+    else in the workspace is the same (d32: 2 GiB of bf16 logits at the default)."""
+    whole = B.gpt_workspace_bytes(configs.D32)
+    chunked = B.gpt_workspace_bytes(configs.D32.replace(ce_chunk_tokens=4096))
+    V, N = configs.D32.vocab, configs.D32.tokens
+    diff = whole - chunked
+    assert abs(diff - (N - 4096) * V * 2) <= 4096, diff
+    # a chunk larger than the batch is the whole batch
+    assert B.gpt_workspace_bytes(configs.TINY.replace(ce_chunk_tokens=1 << 20)) == \
+        B.gpt_workspace_bytes(configs.TINY)
 
 
 def test_init_rejects_missing_or_small_workspace():
@@ -100,7 +114,7 @@ def test_table_entry_point_validation():
     assert L.bigram_fwd(None, 0, 4, 2, 100, None, 1000, 64, B.BF16, None, None, None) == B.GPT_OK
     # bigram_bwd_update: n = 0 is a no-op; too little workspace is refused
     assert L.bigram_bwd_update(None, None, 0, 64, B.BF16, None, None, 10, 0.1, 0.95, 1e-8, None, 0, None) == B.GPT_OK
-    need = L.bigram_workspace_bytes(1000, 64, 1 << 20)
+    need = L.bigram_workspace_bytes(1000, 64)
     assert need > 1000 * 16
     assert L.bigram_bwd_update(16, 16, 1000, 64, B.BF16, 16, 16, 1 << 20, 0.1, 0.95, 1e-8, 256,
                                need - 1, None) == B.GPT_EWORKSPACE
