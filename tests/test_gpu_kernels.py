@@ -164,6 +164,26 @@ def test_rope_qknorm_fwd_bwd(dtype, hd):
         assert rel_l2(host(tdq)[:, blk * D:(blk + 1) * D], want) < tol
 
 
+@pytest.mark.parametrize("dtype", [BF, F32], ids=["bf16", "f32"])
+def test_rope_table_worked_values(dtype):
+    """gptk_rope_table at frequency indices i >= 1 against hand-worked angles t * 10000^(-2i/hd):
+    hd 32, i 8 -> 0.01 per position (t 3: angle 0.03); hd 32, i 4 -> 0.1 (t 5: 0.5); hd 64,
+    i 16 -> 0.01 (t 3: 0.03); each value rounded once to the storage type."""
+    cases = [(32, 8, 3, 0.99955003374898754, 0.029995500202495660),
+             (32, 4, 5, 0.87758256189037276, 0.47942553860420301),
+             (64, 16, 3, 0.99955003374898754, 0.029995500202495660)]
+    for hd, i, t, c, s in cases:
+        cos = torch.empty(8, hd // 2, device="cuda", dtype=dtype)
+        sin = torch.empty_like(cos)
+        B.gptk_rope_table(cos, sin, 8, hd, 10000.0)
+        if dtype == BF:
+            rnd = lambda x: inputs.round_bf16(np.array([x], np.float32))[0]
+        else:
+            rnd = np.float32
+        assert host(cos)[t, i] == rnd(c), (hd, i, t)
+        assert host(sin)[t, i] == rnd(s), (hd, i, t)
+
+
 def _attn_case(dtype, Bn, T, H, hd, seed):
     D = H * hd
     bf = dtype == BF
@@ -177,15 +197,11 @@ def _heads(x, Bn, T, H, hd, blk):
     return x[:, blk * D:(blk + 1) * D].reshape(Bn, T, H, hd).transpose(0, 2, 1, 3)
 
 
-@pytest.mark.parametrize("dtype,hd,T,Bn,H", [(BF, 64, 256, 2, 3), (BF, 128, 192, 2, 3),
-                                              (BF, 32, 64, 2, 3), (F32, 32, 128, 2, 3),
-                                              (F32, 64, 64, 2, 3),
-                                              # >= 512 workgroups: 64 queries per wave
-                                              (BF, 128, 512, 16, 16)])
-def test_attention_fwd_bwd(dtype, hd, T, Bn, H):
+def _check_attention(dtype, hd, T, Bn, H, qkv0):
+    """Forward (out, LSE) and backward (dq, dk, dv) of the kernels against the oracle on the
+    same stored inputs; the backward is fed the oracle's forward results, not the GPU's."""
     D, N = H * hd, Bn * T
     bf = dtype == BF
-    qkv0 = _attn_case(dtype, Bn, T, H, hd, 10)
     tq = dev(qkv0, dtype)
     out = torch.empty(N, D, device="cuda", dtype=dtype)
     lse2 = torch.empty(Bn, H, T, device="cuda")
@@ -215,6 +231,49 @@ def test_attention_fwd_bwd(dtype, hd, T, Bn, H):
     for i, want in enumerate((dq, dk, dv)):
         w = want.transpose(0, 2, 1, 3).reshape(N, D)
         assert rel_l2(got[:, i * D:(i + 1) * D], w) < (2e-2 if bf else 1e-5), i
+    return s
+
+
+@pytest.mark.parametrize("dtype,hd,T,Bn,H", [(BF, 64, 256, 2, 3), (BF, 128, 192, 2, 3),
+                                              (BF, 32, 64, 2, 3), (F32, 32, 128, 2, 3),
+                                              (F32, 64, 64, 2, 3),
+                                              # >= 512 workgroups: 64 queries per wave
+                                              (BF, 128, 512, 16, 16),
+                                              # the d32 sequence length and head size
+                                              (BF, 128, 2048, 1, 2)])
+def test_attention_fwd_bwd(dtype, hd, T, Bn, H):
+    _check_attention(dtype, hd, T, Bn, H, _attn_case(dtype, Bn, T, H, hd, 10))
+
+
+@pytest.mark.parametrize("dtype,hd,T", [(BF, 128, 512), (BF, 64, 512), (BF, 128, 1024),
+                                        (F32, 64, 256), (F32, 32, 256)])
+def test_attention_scores_rising_along_the_sequence(dtype, hd, T):
+    """Keys whose scores rise by ~6 log2 units per 64-key tile: every row's running maximum
+    keeps growing, so the forward's softmax reference maximum (which lags the true maximum
+    until a row's weights would exceed 2^8) must be raised again after the first tile, with a
+    rescale factor strictly between 0 and 1, several times per row at T >= 512.  q_t[0] = 4 and
+    k_s[0] = kappa * s on top of N(0, 1) entries, kappa = 6 sqrt(hd) / (64 * 4 * log2 e)."""
+    Bn, H = 2, 2
+    D = H * hd
+    bf = dtype == BF
+    qkv0 = inputs.normal(15, (Bn * T, 3 * D), 1.0, False)
+    kappa = 6.0 * math.sqrt(hd) / (64 * 4.0 * math.log2(math.e))
+    pos = np.tile(np.arange(T), Bn).astype(np.float64)
+    for h in range(H):
+        qkv0[:, h * hd] = 4.0
+        qkv0[:, D + h * hd] = kappa * pos
+    if bf:
+        qkv0 = inputs.round_bf16(qkv0)
+    s = _check_attention(dtype, hd, T, Bn, H, qkv0)
+    # the inputs do what they are meant to: from the fourth tile on, every query's running
+    # maximum exceeds its maximum over the first tile by more than 8 log2 units (so every wave
+    # rescales after its first tile), and the last rows by more than 3 * 8 when T >= 512
+    l2e = math.log2(math.e)
+    for t in range(192, T, 7):
+        grow = (s[..., t, :t + 1].max(-1) - s[..., t, :64].max(-1)) * l2e
+        assert np.all(grow > 8.0), t
+    if T >= 512:
+        assert np.all((s[..., -1, :].max(-1) - s[..., -1, :64].max(-1)) * l2e > 24.0)
 
 
 def test_attention_single_key_rows_and_constant_keys():

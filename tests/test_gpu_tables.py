@@ -145,17 +145,20 @@ def test_bwd_update_empty_is_noop():
     assert torch.all(table == 1) and torch.all(v == 0)
 
 
-def test_bwd_update_tables_workload():
-    """Tables workload: 196,608 Zipf tokens hashed into the 2^21-row table, dy ~ N(0,1) bf16,
-    lr 1e-2; every touched row checked against the oracle, untouched rows bitwise unchanged."""
+@pytest.mark.parametrize("which", ["x0", "value"])
+def test_bwd_update_tables_workload(which):
+    """Tables workload: 196,608 Zipf tokens hashed into the 2^21-row x0 table or the 2^20-row
+    value table, dy ~ N(0,1) bf16, lr 1e-2; every touched row checked against the oracle,
+    untouched rows bitwise unchanged."""
     tc = configs.TABLES
+    R = tc.x0_rows if which == "x0" else tc.v_rows
     tok = inputs.zipf_tokens(4, (tc.n_tokens // tc.seq_len, tc.seq_len), tc.vocab)
-    h = ot.hash_indices(tok, 2, tc.vocab, tc.x0_rows).reshape(-1).astype(np.int32)
-    dy0 = inputs.normal(204, (tc.n_tokens, tc.dim), 1.0, True)
-    g = torch.Generator(device="cuda").manual_seed(104)
-    table = (torch.randn(tc.x0_rows, tc.dim, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    h = ot.hash_indices(tok, 2, tc.vocab, R).reshape(-1).astype(np.int32)
+    dy0 = inputs.normal(204 if which == "x0" else 205, (tc.n_tokens, tc.dim), 1.0, True)
+    g = torch.Generator(device="cuda").manual_seed(104 if which == "x0" else 106)
+    table = (torch.randn(R, tc.dim, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
     before = table.clone()
-    v = torch.zeros(tc.x0_rows, device="cuda")
+    v = torch.zeros(R, device="cuda")
     _run_update(table, v, dev(h), dev(dy0, torch.bfloat16), tc.lr)
     rows = np.unique(h)
     t_rows = torch.from_numpy(rows).cuda()
@@ -165,7 +168,7 @@ def test_bwd_update_tables_workload():
     assert np.array_equal(r2, np.arange(len(rows)))
     np.testing.assert_allclose(host(v[t_rows]), v_want, rtol=1e-5)
     _check_rows(bf16_bits(table[t_rows]), w0, w_want, v_want, dy0.astype(np.float64), h, tc.lr)
-    mask = torch.ones(tc.x0_rows, dtype=torch.bool, device="cuda")
+    mask = torch.ones(R, dtype=torch.bool, device="cuda")
     mask[t_rows] = False
     assert torch.equal(table[mask], before[mask])
     assert torch.count_nonzero(v[mask]) == 0
