@@ -22,6 +22,7 @@ F32, BF16 = 0, 1
 EXPORTS = [
     "gpt_param_layout", "gpt_workspace_bytes", "gpt_init", "gpt_fwd_bwd", "gpt_check_errors",
     "gpt_profile", "gpt_profile_read", "gpt_destroy", "bigram_fwd", "bigram_workspace_bytes", "bigram_bwd_update",
+    "bigram_bwd_update_noalloc",
     "gpt_last_error", "gpt_status_string", "gpt_opt_state_elems", "gpt_opt_workspace_bytes",
     "gpt_opt_step", "gpt_lr_multiplier", "gpt_muon_momentum", "gpt_infer_workspace_bytes",
     "gpt_infer_init", "gpt_infer_reset", "gpt_infer_position", "gpt_infer_forward",
@@ -90,6 +91,8 @@ def lib() -> C.CDLL:
             "bigram_workspace_bytes": (sz, [i64, i32]),
             "bigram_bwd_update": (i32, [vp, vp, i64, i32, i32, vp, vp, i64, f32, f32, f32, vp,
                                         sz, vp]),
+            "bigram_bwd_update_noalloc": (i32, [vp, vp, i64, i32, i32, vp, vp, i64, f32, f32,
+                                                f32, vp]),
             "gpt_last_error": (C.c_char_p, []),
             "gpt_status_string": (C.c_char_p, [i32]),
             "gptk_gemm": (i32, [i32, i32, i32, i32, i32, i32, vp, i64, vp, i64, vp, i64, i32, vp]),
@@ -261,6 +264,14 @@ def bigram_bwd_update(h, dy, table, v, lr: float, beta2: float = 0.95, eps: floa
     _check(lib().bigram_bwd_update(_ptr(h), _ptr(dy), n, dim, _dtype_code(table), _ptr(table),
                                    _ptr(v), table.shape[0], float(lr), float(beta2), float(eps),
                                    _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def bigram_bwd_update_noalloc(h, dy, table, v, lr: float, beta2: float = 0.95,
+                              eps: float = 1e-8, stream=None):
+    n, dim = dy.shape[0], dy.shape[1]
+    _check(lib().bigram_bwd_update_noalloc(_ptr(h), _ptr(dy), n, dim, _dtype_code(table),
+                                           _ptr(table), _ptr(v), table.shape[0], float(lr),
+                                           float(beta2), float(eps), _stream(stream)))
 
 
 # ---------------------------------------------------------------- per-kernel entry points

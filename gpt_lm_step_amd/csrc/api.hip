@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
@@ -50,6 +51,33 @@ gpt_status prof_read(Prof& pr, gpt_profile_entry* out, int32_t* count, const cha
   *count = (int32_t)agg.size();
   if (out)
     for (int32_t i = 0; i < std::min(cap, *count); ++i) out[i] = agg[i];
+  return GPT_OK;
+}
+
+// Scratch of bigram_bwd_update_noalloc: one copy per GPU, alive until the process ends.  Host
+// code never passes `scratch` itself to a kernel (on the host it names a stand-in, not device
+// memory); it uses the device address hipGetSymbolAddress gives for the current device, looked up
+// once per device on that device's first call and kept here.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+constexpr int NOALLOC_MAX_DEVICES = 64;
+static void* g_scratch_ptr[NOALLOC_MAX_DEVICES];
+static std::mutex g_scratch_mu;
+
+static gpt_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+    return fail(GPT_EHIP, "bigram_bwd_update_noalloc: no usable current device");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(GPT_EHIP, std::string("bigram_bwd_update_noalloc: hipGetSymbolAddress: ") +
+                                hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
   return GPT_OK;
 }
 
@@ -117,6 +145,27 @@ gpt_status bigram_bwd_update(const int32_t* h, const void* dy, int64_t n, int32_
     return segsum_update<float>(h, (const float*)dy, n, dim, (float*)table, v, rows, lr, beta2,
                                 eps, workspace, ws_bytes, stream);
   return fail(GPT_EINVAL, "bigram_bwd_update: bad dtype");
+}
+
+gpt_status bigram_bwd_update_noalloc(const int32_t* h, const void* dy, int64_t n, int32_t dim,
+                                     gpt_dtype dtype, void* table, float* v, int64_t rows,
+                                     float lr, float beta2, float eps, hipStream_t stream) {
+  if (n < 0 || n >= (1LL << 31)) return fail(GPT_ESHAPE, "bigram_bwd_update_noalloc: n out of range");
+  if (n == 0) return GPT_OK;
+  if (dim <= 0 || dim % 8 || dim > 2048)
+    return fail(GPT_ESHAPE, "bigram_bwd_update_noalloc: dim must be a multiple of 8 in [8, 2048]");
+  const size_t need = bigram_workspace_bytes(n, dim);
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(GPT_ESHAPE, "bigram_bwd_update_noalloc: n = " + std::to_string(n) + ", dim = " +
+                                std::to_string(dim) + " needs " + std::to_string(need) +
+                                " bytes of scratch, above its fixed " +
+                                std::to_string(NOALLOC_SCRATCH_BYTES) + " (use bigram_bwd_update)");
+  void* ws = nullptr;
+  gpt_status st = scratch_for_current_device(&ws);
+  if (st != GPT_OK) return st;
+  // Nothing in the scratch has to start at zero: every pass writes what later passes read.
+  return bigram_bwd_update(h, dy, n, dim, dtype, table, v, rows, lr, beta2, eps, ws,
+                           NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

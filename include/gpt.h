@@ -286,6 +286,20 @@ gpt_status bigram_bwd_update(const int32_t* h, const void* dy, int64_t n, int32_
                              float beta2, float eps, void* workspace, size_t ws_bytes,
                              hipStream_t stream);
 
+/* bigram_bwd_update for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation, kernels
+ * and results, with the sort keys, histograms and edge partials in a fixed 32 MiB scratch array
+ * inside the library instead of a caller workspace.  Allocates nothing (no hipMalloc, hipFree or
+ * allocating library call); each GPU the library runs on holds its own copy of the array until
+ * the process ends, looked up on the first call made with that GPU current.  Limit:
+ * bigram_workspace_bytes(n, dim) <= 32 MiB (at dim 768 about 298,000 tokens); larger n returns
+ * GPT_ESHAPE before any launch.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on a GPU (other streams, other host threads) race and must be ordered by the caller.
+ * Arguments and errors otherwise as bigram_bwd_update. */
+gpt_status bigram_bwd_update_noalloc(const int32_t* h, const void* dy, int64_t n, int32_t dim,
+                                     gpt_dtype dtype, void* table, float* v, int64_t rows,
+                                     float lr, float beta2, float eps, hipStream_t stream);
+
 /* Message for the last failing call on this thread [host]; never NULL. */
 const char* gpt_last_error(void);
 const char* gpt_status_string(gpt_status s);
