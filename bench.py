@@ -420,11 +420,17 @@ def bench_tables(a, B):
         gbs = alg[n] / (part_ms[n] / 1e3) / 1e9
         table[n] = {"ms": round(part_ms[n], 4), "algorithmic_bytes": alg[n],
                     "achieved": round(gbs, 1), "unit": "GB/s", "frac": round(gbs * 1e9 / PEAK_HBM, 4)}
-    dom = "gather_x0"  # one kernel per call: its launch duration is the call's
-    roof = {"bound": "hbm", "kernel": "bigram_fwd (hash + gather-add, x0 table)",
+    # the roofline part is the slowest entry point of the step (the x0 table's update: its sort
+    # passes, segmented sums and edge finish are timed together as one call)
+    names = {"gather_x0": "bigram_fwd (hash + gather-add, x0 table)",
+             "gather_v": "bigram_fwd (hash + gather-add, value table)",
+             "update_x0": "bigram_bwd_update (sort + segmented sums + row update, x0 table)",
+             "update_v": "bigram_bwd_update (sort + segmented sums + row update, value table)"}
+    dom = max(table, key=lambda n: table[n]["ms"])
+    roof = {"bound": "hbm", "kernel": names[dom],
             "achieved": table[dom]["achieved"], "peak": PEAK_HBM / 1e9, "unit": "GB/s",
             "frac": table[dom]["frac"],
-            "traffic": measured_traffic("tables", "bigram_fwd (hash + gather-add, x0 table)"),
+            "traffic": measured_traffic("tables", names[dom]),
             "launches_per_step": 1,
             "avg_launch_ms": table[dom]["ms"], "algorithmic_per_launch": alg[dom]}
     out = {
