@@ -32,7 +32,8 @@ EXPORTS = [
 # Every symbol include/gpt_kernels.h declares.
 KERNEL_EXPORTS = [
     "gptk_gemm", "gptk_gemm_wgrad", "gptk_gemm_wgrad_ws_floats", "gptk_rmsnorm_fwd", "gptk_rmsnorm_bwd", "gptk_rope_table",
-    "gptk_rope_qknorm_fwd", "gptk_rope_qknorm_bwd", "gptk_attention_fwd", "gptk_attention_bwd",
+    "gptk_rope_qknorm_fwd", "gptk_rope_qknorm_bwd", "gptk_qkv_rope_fwd", "gptk_attention_fwd",
+    "gptk_attention_bwd",
     "gptk_softcap_ce",
 ]
 
@@ -104,6 +105,8 @@ def lib() -> C.CDLL:
             "gptk_rope_table": (i32, [i32, vp, vp, i32, i32, f32, vp]),
             "gptk_rope_qknorm_fwd": (i32, [i32, vp, vp, vp, vp, i64, i32, i32, i32, i32, f32, vp]),
             "gptk_rope_qknorm_bwd": (i32, [i32, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp]),
+            "gptk_qkv_rope_fwd": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, f32,
+                                        vp]),
             "gptk_attention_fwd": (i32, [i32, vp, vp, vp, i32, i32, i32, i32, vp]),
             "gptk_attention_bwd": (i32, [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]),
             "gptk_softcap_ce": (i32, [i32, vp, i64, vp, i64, i32, f32, f32, vp, vp, vp]),
@@ -323,6 +326,13 @@ def gptk_rope_qknorm_bwd(dqkv, qkv, cos_t, sin_t, rstd_qk, T: int, H: int, hd: i
     _check(lib().gptk_rope_qknorm_bwd(_dtype_code(qkv), _ptr(dqkv), _ptr(qkv), _ptr(cos_t),
                                       _ptr(sin_t), _ptr(rstd_qk), qkv.shape[0], T, H, hd,
                                       qk_norm, _stream(stream)))
+
+
+def gptk_qkv_rope_fwd(x, wqkv, qkv, cos_t, sin_t, rstd_qk, u, T: int, H: int, hd: int,
+                      qk_norm: int = 1, eps: float = 1e-6, stream=None):
+    _check(lib().gptk_qkv_rope_fwd(_ptr(x), _ptr(wqkv), _ptr(qkv), _ptr(cos_t), _ptr(sin_t),
+                                   _ptr(rstd_qk), _ptr(u), x.shape[0], T, H, hd, int(qk_norm),
+                                   float(eps), _stream(stream)))
 
 
 def gptk_attention_fwd(qkv, out, lse2, B: int, T: int, H: int, hd: int, stream=None):

@@ -245,6 +245,91 @@ struct EpiQKV {
   GPT_EPI_CALL
 };
 
+// q/k/v projection with the rotary embedding and the QK-norm applied in the epilogue (the
+// rotation and per-head RMSNorm of CausalSelfAttention.forward on the nanochat page, as
+// rope_qknorm_fwd_kernel computes them, but on the fp32 accumulator instead of a stored bf16
+// product).  Columns [0, D) are q, [D, 2D) k, [2D, 3D) v, head h of a block at h * hd.  For q
+// and k: with t = r mod T and i = column mod hd/2, the first half of a head becomes
+// x1 cos_i + x2 sin_i and the second -x1 sin_i + x2 cos_i; the kernel hands each lane four
+// such pairs of one row (columns c..c+3 and c+hd/2..), hd/8 lanes per head.  With QKN every
+// head is then scaled by r = 1/sqrt(mean(y^2) + eps) and r is saved in rstd_qk [N, 2H] (q
+// heads, then k heads).  v columns get the value addend u (VADD) as EpiQKV does.  Requires
+// wave tiles whose column span is a multiple of hd starting at a multiple of hd, and D a
+// multiple of 128, so that every column test below is wave-uniform.
+template <typename T, bool QKN, bool VADD>
+struct EpiQKVRope {
+  T* out;
+  long long ldo;
+  const T* cos_t;
+  const T* sin_t;
+  float* rstd_qk;
+  const float* u;
+  long long ldu;
+  int D, hd, Tn, H;
+  float eps;
+  static constexpr int wave_cols = 128;  // wave tiles of 128 columns (a head of up to 128)
+  static constexpr bool pairs = true;    // the kernel hands over rotation pairs (see below)
+  struct Pre {
+    vec4t<T> c, s;
+    f32x4 u1, u2;
+  };
+  // Row r; c: column of the first element of four in a head's first half (c2 = c + hd/2 holds
+  // their rotation partners).
+  __device__ __forceinline__ Pre load(int r, int c) const {
+    Pre p;
+    const int half = hd / 2, i = c % hd, t = r % Tn;
+    p.c = *reinterpret_cast<const vec4t<T>*>(cos_t + (long long)t * half + i);
+    p.s = *reinterpret_cast<const vec4t<T>*>(sin_t + (long long)t * half + i);
+    if constexpr (VADD) {
+      // q and k columns read the row's first addend entries and ignore them
+      const float* ur = u + (long long)r * ldu + max(c - 2 * D, 0);
+      p.u1 = *reinterpret_cast<const f32x4*>(ur);
+      p.u2 = *reinterpret_cast<const f32x4*>(ur + (c >= 2 * D ? half : 0));
+    }
+    return p;
+  }
+  __device__ __forceinline__ void store(int r, int c, const float (&x1)[4], const float (&x2)[4],
+                                        const Pre& a) const {
+    float y1[4], y2[4];
+    const int c2 = c + hd / 2;
+    if (c < 2 * D) {  // wave-uniform
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float cs = to_f32(a.c[e]), sn = to_f32(a.s[e]);
+        y1[e] = x1[e] * cs + x2[e] * sn;
+        y2[e] = -x1[e] * sn + x2[e] * cs;
+        ss += y1[e] * y1[e] + y2[e] * y2[e];
+      }
+      if constexpr (QKN) {
+        ss = group_sum(ss, hd / 8);
+        const float rs = 1.f / sqrtf(ss / (float)hd + eps);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          y1[e] *= rs;
+          y2[e] *= rs;
+        }
+        if (c % hd == 0) rstd_qk[(long long)r * 2 * H + c / hd] = rs;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y1[e] = x1[e];
+        y2[e] = x2[e];
+      }
+      if constexpr (VADD) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          y1[e] += a.u1[e];
+          y2[e] += a.u2[e];
+        }
+      }
+    }
+    store4(out + (long long)r * ldo + c, y1);
+    store4(out + (long long)r * ldo + c2, y2);
+  }
+};
+
 // MLP up projection: act = relu(acc)^2 (the only activation the backward needs: the derivative
 // 2 relu(h) equals 2 sqrt(act)).
 template <typename T>
@@ -314,6 +399,24 @@ enum GemmSite {
   G_TRI, G_TRI_WGRAD, G_NS_GRAM, G_NS_POLY, G_NS_APPLY, G_INF_QKV, G_INF_OUT, G_INF_UP,
   G_INF_DOWN, G_INF_HEAD
 };
+
+// Passes of an epilogue row slice whose loads may be in flight together (Epi::pass_group when
+// the epilogue declares one, else all of them), and the wave-tile column span it needs
+// (Epi::wave_cols, else the default 64).
+template <class E, class = void>
+struct epi_pg : std::integral_constant<int, 32> {};
+template <class E>
+struct epi_pg<E, std::void_t<decltype(E::pass_group)>> : std::integral_constant<int, E::pass_group> {};
+template <class E>
+constexpr int epi_pass_group() { return epi_pg<E>::value; }
+template <class E, class = void>
+struct epi_pairs : std::false_type {};
+template <class E>
+struct epi_pairs<E, std::enable_if_t<E::pairs>> : std::true_type {};
+template <class E, class = void>
+struct epi_wave_cols : std::integral_constant<int, 64> {};
+template <class E>
+struct epi_wave_cols<E, std::void_t<decltype(E::wave_cols)>> : std::integral_constant<int, E::wave_cols> {};
 
 // Epilogues of products known to be symmetric (see EpiNsStoreT).
 template <class E, class = void>
@@ -820,8 +923,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
   // reads), then reads them back row-major so that consecutive lanes cover consecutive 4-column
   // groups of one row.  The regions lie in the A halves of the stages.
   static_assert(WTN % 64 == 0, "epilogue staging assumes wave tiles of 64-column multiples");
-  constexpr int REGION = 32 * WTN * 4, WPA = BM * BK * 2 / REGION;
-  static_assert(WPA >= 1 && NS * WPA >= NW, "epilogue staging must fit the stages");
+  constexpr int REGION = 32 * WTN * 4;
+  constexpr int WPA = BM * BK * 2 / REGION, WPB = BN * BK * 2 / REGION;  // regions per half
+  static_assert(NS * (WPA + WPB) >= NW, "epilogue staging must fit the stages");
+  // loads of at most PG passes are in flight together (all of a slice's unless the epilogue
+  // limits it, for the registers its loads take)
+  constexpr int LPR = WTN / 4, RPP = WAVE / LPR, NP = 32 / RPP;
+  constexpr int PG = epi_pass_group<Epi>() < NP ? epi_pass_group<Epi>() : NP;
+  static_assert(NP % PG == 0, "pass groups divide the slice");
   auto epilogue = [&](lds_f32* ep) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -834,24 +943,53 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
           const int chunk = (j * 32 + q * 8 + lg * 4) / 4;
           *reinterpret_cast<lds_f32x4*>(ep + lr * WTN + ((chunk ^ (lr % 16)) * 4)) = v;
         }
-      // all passes' epilogue loads first (at in-range addresses, no per-lane branches), then
-      // the stores
-      constexpr int LPR = WTN / 4, RPP = WAVE / LPR, NP = 32 / RPP;
-      typename Epi::Pre pre[NP];
-      const int c4 = (lane % LPR) * 4, col = n0 + wn + c4;
+      if constexpr (epi_pairs<Epi>::value) {
+        // rotation-pair epilogues: each lane takes four pairs of one row (columns c..c+3 and
+        // c+hd/2..c+hd/2+3 of a head), WTN/8 lanes per row; loads of a whole slice first
+        constexpr int LP2 = WTN / 8, RP2 = WAVE / LP2, NP2 = 32 / RP2;
+        const int hd = epi.hd, jl = lane % LP2, hq = hd / 8;
+        const int cw = (jl / hq) * hd + (jl % hq) * 4;  // column inside the wave tile
+        const int colp = n0 + wn + cw;
+        typename Epi::Pre pre[NP2];
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const int row = m0 + wm + i * 32 + p * RPP + lane / LPR;
-        pre[p] = epi.load(min(row, M - 1), min(col, N - 4));
-      }
+        for (int p = 0; p < NP2; ++p) {
+          const int row = m0 + wm + i * 32 + p * RP2 + lane / LP2;
+          pre[p] = epi.load(min(row, M - 1), colp);
+        }
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const int r = p * RPP + lane / LPR;
-        const f32x4 x = *reinterpret_cast<const lds_f32x4*>(ep + r * WTN + (((c4 / 4) ^ (r % 16)) * 4));
-        const int row = m0 + wm + i * 32 + r;
-        if (row < M && col < N) {
-          const float v[4] = {x[0], x[1], x[2], x[3]};
-          epi.store(row, col, v, pre[p]);
+        for (int p = 0; p < NP2; ++p) {
+          const int r = p * RP2 + lane / LP2;
+          const f32x4 a = *reinterpret_cast<const lds_f32x4*>(ep + r * WTN + (((cw / 4) ^ (r % 16)) * 4));
+          const int cw2 = cw + hd / 2;
+          const f32x4 b = *reinterpret_cast<const lds_f32x4*>(ep + r * WTN + (((cw2 / 4) ^ (r % 16)) * 4));
+          const int row = m0 + wm + i * 32 + r;
+          if (row < M) {
+            const float x1[4] = {a[0], a[1], a[2], a[3]}, x2[4] = {b[0], b[1], b[2], b[3]};
+            epi.store(row, colp, x1, x2, pre[p]);
+          }
+        }
+      } else {
+        // each group's epilogue loads first (at in-range addresses, no per-lane branches), then
+        // its stores
+        const int c4 = (lane % LPR) * 4, col = n0 + wn + c4;
+#pragma unroll
+        for (int p0 = 0; p0 < NP; p0 += PG) {
+          typename Epi::Pre pre[PG];
+#pragma unroll
+          for (int p = 0; p < PG; ++p) {
+            const int row = m0 + wm + i * 32 + (p0 + p) * RPP + lane / LPR;
+            pre[p] = epi.load(min(row, M - 1), min(col, N - 4));
+          }
+#pragma unroll
+          for (int p = 0; p < PG; ++p) {
+            const int r = (p0 + p) * RPP + lane / LPR;
+            const f32x4 x = *reinterpret_cast<const lds_f32x4*>(ep + r * WTN + (((c4 / 4) ^ (r % 16)) * 4));
+            const int row = m0 + wm + i * 32 + r;
+            if (row < M && col < N) {
+              const float v[4] = {x[0], x[1], x[2], x[3]};
+              epi.store(row, col, v, pre[p]);
+            }
+          }
         }
       }
       if constexpr (is_symmetric<Epi>::value) {
@@ -868,13 +1006,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
       }
     }
   };
-  // the region pointer stays in the LDS address space (a generic pointer would turn the
-  // accesses into flat ones, which wait on global memory traffic too)
-  lds_f32* stages[NS];
+  // Wave w stages through region w of the stages' A halves, then of their B halves.  The region
+  // pointer stays in the LDS address space (a generic pointer would turn the accesses into flat
+  // ones, which wait on global memory traffic too).
+  lds_f32* halves[2 * NS];
   static_for<NS>([&](auto s_c) {
-    stages[decltype(s_c)::value] = (lds_f32*)lds_stage<decltype(s_c)::value, BM * BK * 2>();
+    halves[decltype(s_c)::value] = (lds_f32*)lds_stage<decltype(s_c)::value, BM * BK * 2>();
+    halves[NS + decltype(s_c)::value] = (lds_f32*)lds_stage<NS + decltype(s_c)::value, BN * BK * 2>();
   });
-  epilogue(stages[w / WPA] + (w % WPA) * (REGION / 4));
+  if (w < NS * WPA) epilogue(halves[w / WPA] + (w % WPA) * (REGION / 4));
+  else epilogue(halves[NS + (w - NS * WPA) / WPB] + ((w - NS * WPA) % WPB) * (REGION / 4));
 }
 
 // Calls f with an epilogue whose loads do not depend on run-time flags: accumulate vs overwrite
@@ -920,10 +1061,16 @@ void launch_dma(bool a_kc, bool b_kc, int M, int N, int K, const bf16* A, long l
 #define GEMM_DMA(AK, BK_, KT, NS_)                                                               \
   gemm_dma_kernel<BM, BN, WGM, WGN, KT, NS_, AK, BK_, Epi, SITE><<<grid, 64 * WGM * WGN, 0, s>>>( \
       A, lda, B, ldb, M, N, K, ab, bb, epi, kps, a_bs, b_bs)
-  if (a_kc && b_kc) GEMM_DMA(true, true, 64, 2);
-  else if (a_kc) GEMM_DMA(true, false, 64, 2);
-  else if (b_kc) GEMM_DMA(false, true, 32, 4);
-  else GEMM_DMA(false, false, 32, 4);
+  if constexpr (epi_wave_cols<Epi>::value != 64) {
+    // epilogues with wide wave tiles serve forward projections (both operands K-contiguous;
+    // gemm() rejects the other layouts for them)
+    GEMM_DMA(true, true, 64, 2);
+  } else {
+    if (a_kc && b_kc) GEMM_DMA(true, true, 64, 2);
+    else if (a_kc) GEMM_DMA(true, false, 64, 2);
+    else if (b_kc) GEMM_DMA(false, true, 32, 4);
+    else GEMM_DMA(false, false, 32, 4);
+  }
 #undef GEMM_DMA
 }
 
@@ -964,15 +1111,24 @@ inline gpt_status gemm(bool a_kc, bool b_kc, int M, int N, int K, const T* A, lo
   if (gemm_detail::operand_bytes(a_kc, M, K, lda, sizeof(T)) > (1LL << 31) ||
       gemm_detail::operand_bytes(b_kc, N, K, ldb, sizeof(T)) > (1LL << 31))
     return fail(GPT_ESHAPE, "gemm: each operand must span at most 2 GiB");
+  if (epi_wave_cols<Epi>::value != 64 && (!a_kc || !b_kc || !std::is_same<T, bf16>::value))
+    return fail(GPT_EINVAL, "gemm: this epilogue needs bf16 K-contiguous operands");
   const long long big_tiles = (long long)cdiv(M, 256) * cdiv(N, 256);
   if ((long long)cdiv(M, 128) * cdiv(N, 128) >= (1LL << 31)) return fail(GPT_ESHAPE, "gemm: too many tiles");
   gemm_detail::with_static_epi(epi, [&](const auto& e) {
     using E = typename std::decay<decltype(e)>::type;
     if constexpr (std::is_same<T, bf16>::value) {
-      if (big_tiles >= 240)
+      if constexpr (epi_wave_cols<E>::value == 128) {
+        // wave tiles of 64 x 128 (4 x 2 waves) or 32 x 128 (4 x 1)
+        if (big_tiles >= 240)
+          gemm_detail::launch_dma<256, 256, 4, 2, E, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, e, s);
+        else
+          gemm_detail::launch_dma<128, 128, 4, 1, E, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, e, s);
+      } else if (big_tiles >= 240) {
         gemm_detail::launch_dma<256, 256, 2, 4, E, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, e, s);
-      else
+      } else {
         gemm_detail::launch_dma<128, 128, 2, 2, E, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, e, s);
+      }
     } else {
       // fp32 serves the small parity configurations only
       gemm_detail::launch_tiles<T, 64, 64, E, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, e, s);

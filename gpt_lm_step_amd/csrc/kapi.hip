@@ -105,6 +105,28 @@ gpt_status gptk_rope_qknorm_bwd(gpt_dtype dtype, void* dqkv, const void* qkv, co
                                        (const float*)sin_t, rstd_qk, N, T, H, hd, qk_norm, stream);
 }
 
+gpt_status gptk_qkv_rope_fwd(const void* x, const void* wqkv, void* qkv, const void* cos_t,
+                             const void* sin_t, float* rstd_qk, const float* u, int64_t N,
+                             int32_t T, int32_t H, int32_t hd, int32_t qk_norm, float eps,
+                             hipStream_t stream) {
+  if (!x || !wqkv || !qkv || !cos_t || !sin_t || !rstd_qk)
+    return fail(GPT_EINVAL, "gptk_qkv_rope_fwd: null");
+  gpt_status st = check_heads(N, T, H, hd);
+  if (st != GPT_OK || N == 0) return st;
+  const int D = H * hd;
+  if (D % 128) return fail(GPT_ESHAPE, "gptk_qkv_rope_fwd: H * hd must be a multiple of 128");
+  if (((uintptr_t)qkv | (uintptr_t)u) % 16) return fail(GPT_EINVAL, "gptk_qkv_rope_fwd: misaligned");
+  auto go = [&](auto qkn_c, auto vadd_c) {
+    constexpr bool QKN = decltype(qkn_c)::value, VADD = decltype(vadd_c)::value;
+    const EpiQKVRope<bf16, QKN, VADD> e{(bf16*)qkv, 3LL * D, (const bf16*)cos_t,
+                                        (const bf16*)sin_t, rstd_qk, u, D, D, hd, T, H, eps};
+    return gemm<G_TEST, bf16>(true, true, (int)N, 3 * D, D, (const bf16*)x, D,
+                              (const bf16*)wqkv, D, e, stream);
+  };
+  if (qk_norm) return u ? go(std::true_type(), std::true_type()) : go(std::true_type(), std::false_type());
+  return u ? go(std::false_type(), std::true_type()) : go(std::false_type(), std::false_type());
+}
+
 gpt_status gptk_attention_fwd(gpt_dtype dtype, const void* qkv, void* out, float* lse2, int32_t B,
                               int32_t T, int32_t H, int32_t hd, hipStream_t stream) {
   if (bad_dtype(dtype) || !qkv || !out || !lse2) return fail(GPT_EINVAL, "gptk_attention_fwd: null");

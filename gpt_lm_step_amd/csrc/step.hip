@@ -6,6 +6,7 @@
 
 #include <string>
 #include <algorithm>
+#include <type_traits>
 #include <vector>
 
 #include "gemm.h"
@@ -222,6 +223,26 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
         launch_embed_fwd<T>(tokens, P + Ly.wte, c.has_x0_add ? x0_add : nullptr, p.L[0].x_in,
                             p.e_rstd, p.tok_c, p.err, N, D, V, eps, s));
 
+  // The bf16 path applies rotary + QK-norm in the QKV projection's epilogue when every wave
+  // tile of 128 projection columns lies inside one of the q, k, v blocks (d_model a multiple of
+  // 128); otherwise (and on the fp32 path) the projection is stored and a separate kernel
+  // rotates and normalizes q and k in place.  Both leave the same tensors for the backward.
+  const bool fuse_rope = std::is_same<T, bf16>::value && D % 128 == 0;
+  auto qkv_rope = [&](const T* w, const T* a, T* qkv, float* rstd_qk) -> gpt_status {
+    if constexpr (std::is_same<T, bf16>::value) {
+      auto go = [&](auto qkn_c, auto vadd_c) {
+        constexpr bool QKN = decltype(qkn_c)::value, VADD = decltype(vadd_c)::value;
+        const EpiQKVRope<T, QKN, VADD> e{qkv, 3LL * D, cos_t, sin_t, rstd_qk, u, D, D, hd, Tn,
+                                         H, eps};
+        return gemm<G_QKV, T>(true, true, (int)N, 3 * D, D, a, D, w, D, e, s);
+      };
+      if (c.qk_norm) return u ? go(std::true_type(), std::true_type()) : go(std::true_type(), std::false_type());
+      return u ? go(std::false_type(), std::true_type()) : go(std::false_type(), std::false_type());
+    } else {
+      return fail(GPT_EINVAL, "fused rotary projection is bf16 only");
+    }
+  };
+
   // ---------------- forward
   for (int l = 0; l < Lc; ++l) {
     LayerBufs& b = p.L[l];
@@ -229,11 +250,17 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
     float* x_out = l + 1 < Lc ? p.L[l + 1].x_in : p.x_final;
     STAGE("rmsnorm_fwd", 0, ND * (4 + es) + 4.0 * N,
           launch_rms_fwd<T>(b.x_in, a, b.rstd_a, N, D, eps, s));
-    STAGE("qkv_fwd", mm(N, 3 * D, D), 0,
-          gemm<G_QKV, T>(true, true, (int)N, 3 * D, D, a, D, P + Ly.wqkv[l], D,
-                         EpiQKV<T>{qkv, 3LL * D, u, D, 2 * D}, s));
-    STAGE("rope_qknorm_fwd", 0, 4.0 * ND * es + 8.0 * N * H,
-          launch_rope_qknorm_fwd<T>(qkv, cos_t, sin_t, b.rstd_qk, N, Tn, H, hd, c.qk_norm, eps, s));
+    if (fuse_rope) {
+      // rotary + QK-norm in the projection's epilogue: one pass, q and k never stored unrotated
+      STAGE("qkv_rope_fwd", mm(N, 3 * D, D), 0,
+            qkv_rope(P + Ly.wqkv[l], a, qkv, b.rstd_qk));
+    } else {
+      STAGE("qkv_fwd", mm(N, 3 * D, D), 0,
+            gemm<G_QKV, T>(true, true, (int)N, 3 * D, D, a, D, P + Ly.wqkv[l], D,
+                           EpiQKV<T>{qkv, 3LL * D, u, D, 2 * D}, s));
+      STAGE("rope_qknorm_fwd", 0, 4.0 * ND * es + 8.0 * N * H,
+            launch_rope_qknorm_fwd<T>(qkv, cos_t, sin_t, b.rstd_qk, N, Tn, H, hd, c.qk_norm, eps, s));
+    }
     STAGE("attn_fwd", 4.0 * pairs * hd, 0, launch_attn_fwd<T>(qkv, o, b.lse, Bn, Tn, H, hd, s));
     STAGE("out_fwd", mm(N, D, D), 0,
           gemm<G_OUT, T>(true, true, (int)N, D, D, o, D, P + Ly.wo[l], D,

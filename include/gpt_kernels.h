@@ -62,7 +62,18 @@ gpt_status gptk_rope_qknorm_bwd(gpt_dtype dtype, void* dqkv, const void* qkv, co
                                 const void* sin_t, const float* rstd_qk, int64_t N, int32_t T,
                                 int32_t H, int32_t hd, int32_t qk_norm, hipStream_t stream);
 
-/* Causal attention forward (F.scaled_dot_product_attention(is_causal=True) in the nanochat
+/* The q/k/v projection with rotary + QK-norm in its epilogue (bf16 only), as the bf16 step runs
+ * it when H * hd is a multiple of 128: qkv bf16 [N, 3D] = x [N, D] wqkv^T ([3D, D]), then on the
+ * q and k blocks the half-split rotation of apply_rotary_emb with the tables of
+ * gptk_rope_table (position t = row mod T) and, if qk_norm, RMSNorm per head with rstd_qk
+ * fp32 [N, 2H] (q heads then k heads); v columns get u fp32 [N, D] when u is not NULL.  The
+ * rotation acts on the fp32 products (the two-kernel form rotates their bf16 rounding). */
+gpt_status gptk_qkv_rope_fwd(const void* x, const void* wqkv, void* qkv, const void* cos_t,
+                             const void* sin_t, float* rstd_qk, const float* u, int64_t N,
+                             int32_t T, int32_t H, int32_t hd, int32_t qk_norm, float eps,
+                             hipStream_t stream);
+
+/* Causal attention forward/* Causal attention forward (F.scaled_dot_product_attention(is_causal=True) in the nanochat
  * GPT class): qkv T [B*T, 3D] -> out T [B*T, D], lse2 fp32 [B, H, T] = log2 sum_s
  * 2^(q.k_s * log2(e)/sqrt(hd)) (base-2 log-sum-exp of the scaled scores). */
 gpt_status gptk_attention_fwd(gpt_dtype dtype, const void* qkv, void* out, float* lse2, int32_t B,

@@ -344,3 +344,38 @@ def test_cross_entropy_rows_per_workgroup(dtype, V, rows, cap):
     per_row = np.linalg.norm(g - g_want / nv, axis=1) / np.maximum(np.linalg.norm(g_want / nv, axis=1), 1e-30)
     assert np.max(per_row[tgt >= 0]) < (2e-2 if bf else 1e-4)
     assert np.all(g[tgt < 0] == 0)
+
+
+@pytest.mark.parametrize("hd,H,T,Bn,qk_norm,vadd", [(128, 2, 64, 5, 1, False),   # 128x128 tiles, ragged M
+                                                   (64, 4, 128, 3, 0, True),
+                                                   (32, 4, 64, 4, 1, True),
+                                                   (128, 16, 64, 41, 1, False)])  # 256x256, ragged M
+def test_qkv_projection_with_fused_rotary_qknorm(hd, H, T, Bn, qk_norm, vadd):
+    """The bf16 q/k/v projection with rotary + QK-norm in the GEMM epilogue against the oracle:
+    q = x Wq^T etc. in fp64, the half-split rotation with the stored (bf16) tables, RMSNorm per
+    head; rstd per (token, head); the value block plus its addend."""
+    D = H * hd
+    N = Bn * T
+    x = inputs.normal(16, (N, D), 1.0, True)
+    w = inputs.normal(17, (3 * D, D), 0.05, True)
+    u = inputs.normal(18, (N, D), 0.5, False) if vadd else None
+    cos = torch.empty(T, hd // 2, device="cuda", dtype=BF)
+    sin = torch.empty_like(cos)
+    B.gptk_rope_table(cos, sin, T, hd, 10000.0)
+    qkv = torch.full((N, 3 * D), float("nan"), device="cuda", dtype=BF)
+    rstd = torch.full((N, 2 * H), float("nan"), device="cuda")
+    B.gptk_qkv_rope_fwd(dev(x, BF), dev(w, BF), qkv, cos, sin, rstd, None if u is None else dev(u),
+                        T, H, hd, qk_norm, 1e-6)
+    torch.cuda.synchronize()
+    y = x.astype(np.float64) @ w.astype(np.float64).T
+    cq, sq = host(cos).astype(np.float64), host(sin).astype(np.float64)
+    got = host(qkv)
+    for blk in (0, 1):
+        z = om.rope(y[:, blk * D:(blk + 1) * D].reshape(Bn, T, H, hd), cq, sq)
+        if qk_norm:
+            z, r = om.rms_norm(z, 1e-6)
+            np.testing.assert_allclose(host(rstd)[:, blk * H:(blk + 1) * H], r.reshape(N, H),
+                                       rtol=1e-4)
+        assert rel_l2(got[:, blk * D:(blk + 1) * D], z.reshape(N, D)) < 4e-3, blk
+    v = y[:, 2 * D:] + (u.astype(np.float64) if vadd else 0.0)
+    assert rel_l2(got[:, 2 * D:], v) < 4e-3
