@@ -242,10 +242,13 @@ __device__ __forceinline__ void store_acc_rows(T* __restrict__ dst_row, const f3
 // bf16 (NWV = 8, two waves per SIMD): K and V as swizzled row tiles (V^T by transposing reads),
 // staged by the two halves of the workgroup.  fp32 (NWV = 4): threads 0..127 move K (padded
 // rows), 128..255 move V (transposed).
-template <typename T, int HD, int NWV>
+// BOUNDED: every score is at most `bound` (q and k RMS-normalized per head, so |q.k|/sqrt(Hd) <=
+// sqrt(Hd)): the softmax weights are taken against that fixed reference, 2^(sl2 (s - bound)) in
+// [2^(-2 sl2 bound), 1], and no running maximum is kept.
+template <typename T, int HD, int NWV, bool BOUNDED>
 __global__ __launch_bounds__(64 * NWV, NWV == 8 ? 1 : 2) void attn_fwd_kernel(
     const T* __restrict__ qkv, T* __restrict__ out, float* __restrict__ lse2, int Tn, int H,
-    float sl2) {
+    float sl2, float bound) {
   constexpr int BKV = 64, BQ = 32 * NWV, PK = HD + pad<T>(), PV = BKV + pad<T>();
   constexpr bool SW = sizeof(T) == 2;
   static_assert(SW || NWV == 4, "the fp32 staging assumes 4 waves");
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 8 ? 1 : 2) void attn_fwd_kernel(
   const int q0 = qb * BQ + w * 32, q = q0 + lr;
   vec8_t<T> qf[HD / 16];
   f32x16 o[HD / 32];
-  float m = -INFINITY, l = 0.f;
+  float m = BOUNDED ? bound : -INFINITY, l = 0.f;
   {
     const int qq = min(q, Tn - 1);
 #pragma unroll
@@ -318,32 +321,37 @@ __global__ __launch_bounds__(64 * NWV, NWV == 8 ? 1 : 2) void attn_fwd_kernel(
           else mma<T>(sc[st2], frag_rows(K_, PK, st2 * 32 + lr, c * 16, g), qf[c]);
         }
       }
-      float mx = -INFINITY;
+      if (DIAG) {
 #pragma unroll
-      for (int st2 = 0; st2 < 2; ++st2)
+        for (int st2 = 0; st2 < 2; ++st2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (DIAG) {
+          for (int r = 0; r < 16; ++r) {
             const int key = kv0 + st2 * 32 + (r / 4) * 8 + g * 4 + (r % 4);
             if (key > q) sc[st2][r] = -INFINITY;
           }
-          mx = fmaxf(mx, sc[st2][r]);
+      }
+      if constexpr (!BOUNDED) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[st2][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+        // The reference max m may lag the true running max: weights are 2^(sl2 (s - m)), so O,
+        // l and the saved LSE2 = sl2 m + log2 l all refer to the same m and the result is exact
+        // whatever m is, as long as the weights stay in range.  m is raised (and O, l rescaled)
+        // only when some row's scores exceed it by more than 2^8 in weight, which after the
+        // first tile is rare, instead of on every tile where some row's max moves.
+        if (!__all((mx - m) * sl2 <= 8.f)) {  // also taken on the first tile (m = -inf)
+          const float mn = fmaxf(m, mx);
+          const float alpha = fast_exp2((m - mn) * sl2);  // 0 on the first tile, 1 where unchanged
+#pragma unroll
+          for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+          l *= alpha;
+          m = mn;
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-      // The reference max m may lag the true running max: weights are 2^(sl2 (s - m)), so O, l
-      // and the saved LSE2 = sl2 m + log2 l all refer to the same m and the result is exact
-      // whatever m is, as long as the weights stay in range.  m is raised (and O, l rescaled)
-      // only when some row's scores exceed it by more than 2^8 in weight, which after the first
-      // tile is rare, instead of on every tile where some row's max moves.
-      if (!__all((mx - m) * sl2 <= 8.f)) {  // also taken on the first tile (m = -inf)
-        const float mn = fmaxf(m, mx);
-        const float alpha = fast_exp2((m - mn) * sl2);  // 0 on the first tile, 1 where unchanged
-#pragma unroll
-        for (int dt = 0; dt < HD / 32; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-        l *= alpha;
-        m = mn;
       }
       const float nb = -m * sl2;
       float sum = 0.f;
@@ -1036,15 +1044,21 @@ gpt_status dispatch_hd(int hd, F&& f) {
 
 template <typename T>
 gpt_status launch_attn_fwd(const T* qkv, T* out, float* lse2, int B, int Tn, int H, int hd,
-                           hipStream_t s) {
+                           hipStream_t s, int qk_normed) {
   const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
+  // With q and k RMS-normalized per head, |q| and |k| are at most sqrt(hd) (times 1 + 2^-8
+  // after bf16 rounding), so every scaled score is at most sqrt(hd) (1 + 2^-7).
+  const float bound = sqrtf((float)hd) * (1.f + 1.f / 128.f);
   // 32 queries per wave, two waves per SIMD so that one wave's softmax overlaps the other's
   // MFMAs: bf16 runs 8-wave workgroups (one per CU), fp32 4-wave workgroups (two per CU).
   gpt_status st = dispatch_hd<T>(hd, [&](auto HD) {
     constexpr int hdv = decltype(HD)::value;
     constexpr int NWV = sizeof(T) == 2 ? 8 : 4;
-    attn_fwd_kernel<T, hdv, NWV><<<dim3(H * B, cdiv(Tn, 32 * NWV)), 64 * NWV, 0, s>>>(
-        qkv, out, lse2, Tn, H, sl2);
+    const dim3 grid(H * B, cdiv(Tn, 32 * NWV));
+    if (qk_normed)
+      attn_fwd_kernel<T, hdv, NWV, true><<<grid, 64 * NWV, 0, s>>>(qkv, out, lse2, Tn, H, sl2, bound);
+    else
+      attn_fwd_kernel<T, hdv, NWV, false><<<grid, 64 * NWV, 0, s>>>(qkv, out, lse2, Tn, H, sl2, bound);
   });
   return st != GPT_OK ? st : check_launch("attention fwd");
 }
@@ -1093,9 +1107,9 @@ gpt_status launch_attn_bwd(const T* qkv, const T* out, const T* dout, const floa
 }
 
 template gpt_status launch_attn_fwd<float>(const float*, float*, float*, int, int, int, int,
-                                           hipStream_t);
+                                           hipStream_t, int);
 template gpt_status launch_attn_fwd<bf16>(const bf16*, bf16*, float*, int, int, int, int,
-                                          hipStream_t);
+                                          hipStream_t, int);
 template gpt_status launch_attn_bwd<float>(const float*, const float*, const float*, const float*,
                                            float*, float*, int, int, int, int, hipStream_t);
 template gpt_status launch_attn_bwd<bf16>(const bf16*, const bf16*, const bf16*, const float*,

@@ -695,7 +695,7 @@ gpt_status infer_forward(gpt_infer* c, const T* P, const int32_t* tokens, int B,
       // a first chunk: the training kernel's causal pass over the chunk itself
       const double pairs = (double)B * H * Tn * (Tn + 1) / 2.0;
       TRY(run("attention", 4.0 * pairs * hd, Md * 4 * D * es,
-              [&] { return launch_attn_fwd<T>(qkv, att, c->lse2, B, Tn, H, hd, s); }));
+              [&] { return launch_attn_fwd<T>(qkv, att, c->lse2, B, Tn, H, hd, s, g.qk_norm); }));
     } else {
       // queries over the cache, AS_MAX_T at a time
       const float scale = 1.f / sqrtf((float)hd);

@@ -89,9 +89,11 @@ gpt_status launch_loss_reduce(const float* loss_rows, long long N, const int* n_
                               float* loss, hipStream_t s);
 
 // ---------------------------------------------------------------- attention (attn.hip)
+// qk_normed: q and k are RMS-normalized per head (the QK-norm), which bounds every score, so
+// the softmax needs no running maximum.
 template <typename T>
 gpt_status launch_attn_fwd(const T* qkv, T* out, float* lse2, int B, int Tn, int H, int hd,
-                           hipStream_t s);
+                           hipStream_t s, int qk_normed = 0);
 // stage 0: rowsum(dO * O) into dq_sum and dQ; stage 1: dK, dV (reads dq_sum).
 template <typename T>
 gpt_status launch_attn_bwd_stage(int stage, const T* qkv, const T* out, const T* dout,

@@ -261,7 +261,8 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
       STAGE("rope_qknorm_fwd", 0, 4.0 * ND * es + 8.0 * N * H,
             launch_rope_qknorm_fwd<T>(qkv, cos_t, sin_t, b.rstd_qk, N, Tn, H, hd, c.qk_norm, eps, s));
     }
-    STAGE("attn_fwd", 4.0 * pairs * hd, 0, launch_attn_fwd<T>(qkv, o, b.lse, Bn, Tn, H, hd, s));
+    STAGE("attn_fwd", 4.0 * pairs * hd, 0,
+          launch_attn_fwd<T>(qkv, o, b.lse, Bn, Tn, H, hd, s, c.qk_norm));
     STAGE("out_fwd", mm(N, D, D), 0,
           gemm<G_OUT, T>(true, true, (int)N, D, D, o, D, P + Ly.wo[l], D,
                          EpiResid{b.x_in, b.x_mid, D}, s));
