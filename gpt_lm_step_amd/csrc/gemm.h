@@ -1216,8 +1216,9 @@ inline long long gemm_wgrad_ws_floats(int M, int N, int K) {
   return sp.splits > 1 ? (long long)sp.splits * M * N : 0;
 }
 
-// Weight-gradient GEMM (fp32 output, beta as in EpiStoreF32): bf16 shapes that leave CUs idle
-// are split over K into fp32 partials in `ws` and reduced in split order (deterministic).
+// GEMM with an fp32 output (weight gradients, and the input gradients that feed the fp32
+// residual stream; beta as in EpiStoreF32): bf16 shapes that leave CUs idle are split over K
+// into fp32 partials in `ws` and reduced in split order (deterministic).
 template <int SITE, typename T>
 inline gpt_status gemm_wgrad(bool a_kc, bool b_kc, int M, int N, int K, const T* A, long long lda,
                              const T* B, long long ldb, const EpiStoreF32& epi, float* ws,

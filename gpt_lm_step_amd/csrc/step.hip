@@ -147,7 +147,9 @@ Plan carve_plan(const gpt_config& c, Carver& cv) {
     const int n = (int)N, d = (int)D, f = (int)F;
     const long long need[] = {gemm_wgrad_ws_floats(3 * d, d, n), gemm_wgrad_ws_floats(d, d, n),
                               gemm_wgrad_ws_floats(d, f, n), gemm_wgrad_ws_floats(f, d, n),
-                              gemm_wgrad_ws_floats(c.vocab, d, (int)p.ce_rows)};
+                              gemm_wgrad_ws_floats(c.vocab, d, (int)p.ce_rows),
+                              // the LM head's input gradient (fp32 output, K = vocab)
+                              gemm_wgrad_ws_floats((int)p.ce_rows, d, c.vocab)};
     for (long long x : need) p.splitk_floats = std::max(p.splitk_floats, x);
   }
   p.splitk = p.splitk_floats ? cv.take<float>(p.splitk_floats) : nullptr;
@@ -290,8 +292,9 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
           launch_ce<T>(z, V, targets + c0, rows, V, c.softcap, grad_scale, p.n_valid,
                        p.loss_rows + c0, s));
     STAGE("head_dgrad", mm(rows, D, V), 0,
-          gemm<G_HEAD_DGRAD, T>(true, false, rows, D, V, z, V, wh, D,
-                                EpiStoreF32{p.df + c0 * D, D, 0}, s));
+          gemm_wgrad<G_HEAD_DGRAD, T>(true, false, rows, D, V, z, V, wh, D,
+                                      EpiStoreF32{p.df + c0 * D, D, 0}, p.splitk,
+                                      p.splitk_floats, s));
     STAGE("head_wgrad", mm(V, D, rows), 0,
           gemm_wgrad<G_HEAD_WGRAD, T>(false, false, V, D, rows, z, V, f + c0 * D, D,
                                       EpiStoreF32{G + Ly.lm_head, D, (beta || c0 > 0) ? 1 : 0},
