@@ -1,5 +1,6 @@
 // Matrix-core GEMMs of the step (q/k/v, out, MLP up/down and LM-head projections and their
-// input- and weight-gradients), hand-written for gfx950.
+// input- and weight-gradients, the Newton-Schulz products of the optimizer, the prefill
+// products of inference), hand-written for gfx950.
 //
 //   C[m, n] = sum_k A(m, k) * B(n, k)
 //
@@ -7,19 +8,24 @@
 // ("RC": element (r, k) at p[k*ld + r]).  Forward projections y = x W^T are KC x KC; input
 // gradients dx = dy W are KC x RC; weight gradients dW = dy^T x are RC x RC.
 //
-// Design (one 256-thread workgroup per 128x128 output tile, 4 waves of 64x64):
-//  * tiles of A and B are staged through LDS as [row][k] with 16 bytes of padding per row;
-//    global loads are 16 B vectors, coalesced along the contiguous dimension; RC operands are
-//    transposed on the way in by an 8x8 in-register transpose, so both layouts feed the same
-//    LDS format;
-//  * the next K tile is loaded into registers while the current one is multiplied (two LDS
-//    buffers, one barrier per K step);
-//  * bf16 uses v_mfma_f32_32x32x16_bf16, fp32 uses v_mfma_f32_32x32x2f32 (8 per 16-wide K
-//    slice); both take 8 consecutive K values per lane, so operand fragments are identical;
-//  * the tile order keeps each XCD on a contiguous block of output tiles (L2 reuse), grouped
-//    along M so neighbouring tiles share operand panels;
-//  * epilogues are fused: bf16/fp32 stores, value addend, ReLU^2,
-//    dReLU^2, residual add, and beta-accumulation for weight gradients.
+// bf16 (gemm_dma_kernel): one workgroup per 256 x 256 output tile (8 waves, two per SIMD, each
+// 128 x 64 or 64 x 128) when that tiling has enough tiles to fill the GPU, else 128 x 128 (4
+// waves, two workgroups per CU):
+//  * operand tiles travel global -> LDS by LDS-DMA buffer loads in the operand's own layout
+//    (XOR-swizzled, no staging registers, no LDS store instructions); RC tiles are read back
+//    with transposing LDS reads; loads past an operand's end read zeros (buffer range check);
+//  * K advances through a ring of LDS stages: two 64-wide stages when A is K-contiguous (whole
+//    128-byte lines per DMA row), four 32-wide stages otherwise; one barrier per K tile, the
+//    next tile's first fragments read during the current tile's last MFMAs;
+//  * v_mfma_f32_32x32x16_bf16 with the B fragment first, so each lane ends with 4 consecutive
+//    output columns; the epilogue stages 32-row slices through LDS and stores coalesced rows;
+//  * epilogues are fused: bf16/fp32 stores, value addend, rotary + QK-norm (EpiQKVRope), ReLU^2,
+//    dReLU^2, residual add, beta-accumulation, split-K partials, Newton-Schulz combinations;
+//  * blocks are dispatched round-robin over the 8 XCDs; each XCD walks a contiguous range of
+//    tiles in groups of 8 row tiles (operand panels shared in its L2);
+//  * shapes whose tiling leaves CUs idle and that have an fp32 output (weight gradients, the LM
+//    head's input gradient) split K into fp32 partials reduced in split order (deterministic).
+// fp32 (gemm_kernel, the parity configurations only): 64 x 64 tiles staged through registers.
 // Header-only: every call site instantiates its own kernel symbol (a GemmSite tag), so
 // profiles name the projection a launch belongs to.
 #pragma once
@@ -545,10 +551,11 @@ __device__ __forceinline__ void tri_coords(int T, int& tm, int& tn) {
   tn = r + L;
 }
 
-// BM x BN output tile per workgroup; each wave computes (BM/2) x (BN/2) as (BM/64) x (BN/64)
-// MFMA tiles of 32 x 32, so every 16-wide K slice reads BM/64 + BN/64 fragments from LDS for
-// (BM/64) * (BN/64) MFMAs.  The 256 x 256 tile keeps 256 accumulators per lane (AGPRs) and
-// runs one workgroup per CU with both LDS buffers (147 KB).
+// Register-staged kernel, launched for fp32 operands (the parity configurations) with 64 x 64
+// tiles: BM x BN output tile per workgroup, each wave computing (BM/2) x (BN/2) as (BM/64) x
+// (BN/64) MFMA tiles of 32 x 32 (v_mfma_f32_32x32x2f32, eight per 16-wide K slice); operand
+// tiles go global -> registers -> LDS (padded rows; RC operands transposed in registers), the
+// next K tile loaded into registers while the current one is multiplied.
 template <typename T, int BM, int BN, bool A_KC, bool B_KC, class Epi, int SITE>
 __global__ __launch_bounds__(THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_kernel(
     const T* __restrict__ A, long long lda, const T* __restrict__ B, long long ldb, int M, int N,
