@@ -139,7 +139,7 @@ Plan carve_plan(const gpt_config& c, Carver& cv) {
   p.df = cv.take<float>(N * D);
   p.loss_rows = cv.take<float>(N);
   p.n_valid = cv.take<int>(64);
-  p.err = p.n_valid + 16;
+  p.err = p.n_valid ? p.n_valid + 16 : nullptr;  // sizing carves hand out null pointers
   p.seg_bytes = segsum_workspace_bytes(N, (int)D);
   p.seg_ws = cv.take<char>(p.seg_bytes);
   p.splitk_floats = 0;

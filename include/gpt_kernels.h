@@ -73,7 +73,7 @@ gpt_status gptk_qkv_rope_fwd(const void* x, const void* wqkv, void* qkv, const v
                              int32_t T, int32_t H, int32_t hd, int32_t qk_norm, float eps,
                              hipStream_t stream);
 
-/* Causal attention forward/* Causal attention forward (F.scaled_dot_product_attention(is_causal=True) in the nanochat
+/* Causal attention forward (F.scaled_dot_product_attention(is_causal=True) in the nanochat
  * GPT class): qkv T [B*T, 3D] -> out T [B*T, D], lse2 fp32 [B, H, T] = log2 sum_s
  * 2^(q.k_s * log2(e)/sqrt(hd)) (base-2 log-sum-exp of the scaled scores). */
 gpt_status gptk_attention_fwd(gpt_dtype dtype, const void* qkv, void* out, float* lse2, int32_t B,
