@@ -2,6 +2,8 @@
 // 64-wide wavefront reductions and the host-side status plumbing.
 #pragma once
 
+#include <vector>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -127,17 +129,29 @@ gpt_status check_launch(const char* what);
 inline unsigned cdiv(long long a, long long b) { return (unsigned)((a + b - 1) / b); }
 inline size_t align_up(size_t n, size_t a = 256) { return (n + a - 1) / a * a; }
 
-// Bump allocator over a caller-provided workspace.  With base == nullptr it only measures
-// (size() is then the bytes a real carve needs).
+// Bump allocator over a caller-provided workspace: hands out consecutive 256-byte aligned
+// regions (with a null base it only measures: size() is then the bytes a real carve needs).
+// With `guard` set, every region is followed by a GUARD_BYTES guard region whose offset is
+// recorded in `guards` (filled with a known pattern and checked later, so a kernel writing
+// past the end of its buffer is detected).
+constexpr size_t GUARD_BYTES = 256;
+constexpr uint32_t GUARD_WORD = 0xA5C3F00Du;
 struct Carver {
   char* base;
   size_t cap, off = 0;
   bool ok = true;
+  bool guard = false;
+  std::vector<size_t> guards;
   Carver(void* b, size_t c) : base((char*)b), cap(c) {}
   template <typename T>
   T* take(size_t n) {
     size_t at = align_up(off);
     off = at + n * sizeof(T);
+    if (guard) {
+      const size_t g = align_up(off);
+      guards.push_back(g);
+      off = g + GUARD_BYTES;
+    }
     if (base == nullptr) return nullptr;
     if (off > cap) { ok = false; return nullptr; }
     return (T*)(base + at);

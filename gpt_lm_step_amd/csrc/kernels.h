@@ -73,6 +73,10 @@ gpt_status launch_rope_qknorm_bwd(T* dqkv, const T* qkv, const T* cos_t, const T
                                   const float* rstd_qk, long long N, int Tn, int H, int hd,
                                   int qk_norm, hipStream_t s);
 gpt_status launch_fill(float* p, long long n, float v, hipStream_t s);
+// Workspace guards (Carver): check == 0 writes GUARD_WORD over the n guards listed in tab
+// (byte offsets into ws); check == 1 sets bit 4 of *err if any guard word differs.
+gpt_status launch_guards(char* ws, const long long* tab, int n, int* err, int check,
+                         hipStream_t s);
 template <typename T>
 gpt_status launch_accum_rows(float* dst, const T* src, long long lds, long long N, int D, int add,
                              hipStream_t s);

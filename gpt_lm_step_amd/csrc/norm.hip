@@ -277,6 +277,19 @@ __global__ __launch_bounds__(256) void rope_qknorm_bwd_kernel(
   store8_f32(dqkv + off + i + half, o2);
 }
 
+// ------------------------------------------------------------------ workspace guards
+// Guard g of the table covers bytes [tab[g], tab[g] + GUARD_BYTES) of the workspace; one
+// workgroup per guard, one 32-bit word per thread.
+__global__ void guard_fill_kernel(char* __restrict__ ws, const long long* __restrict__ tab) {
+  uint32_t* w = reinterpret_cast<uint32_t*>(ws + tab[blockIdx.x]);
+  w[threadIdx.x] = GUARD_WORD;
+}
+__global__ void guard_check_kernel(const char* __restrict__ ws, const long long* __restrict__ tab,
+                                   int* __restrict__ err) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(ws + tab[blockIdx.x]);
+  if (w[threadIdx.x] != GUARD_WORD) atomicOr(err, 4);
+}
+
 // ------------------------------------------------------------------ elementwise helpers
 __global__ void fill_f32_kernel(float* p, long long n, float v) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -392,6 +405,15 @@ gpt_status launch_rope_qknorm_bwd(T* dqkv, const T* qkv, const T* cos_t, const T
   rope_qknorm_bwd_kernel<T><<<cdiv(N * H * hd / 8, 256), 256, 0, s>>>(dqkv, qkv, cos_t, sin_t,
                                                                       rstd_qk, N, Tn, H, hd, qk_norm);
   return check_launch("rope+qknorm bwd");
+}
+
+gpt_status launch_guards(char* ws, const long long* tab, int n, int* err, int check,
+                         hipStream_t s) {
+  if (n == 0) return GPT_OK;
+  constexpr int W = (int)(GUARD_BYTES / 4);
+  if (check) guard_check_kernel<<<n, W, 0, s>>>(ws, tab, err);
+  else guard_fill_kernel<<<n, W, 0, s>>>(ws, tab);
+  return check_launch("workspace guards");
 }
 
 gpt_status launch_fill(float* p, long long n, float v, hipStream_t s) {

@@ -94,11 +94,20 @@ struct Plan {
   float* splitk;             // split-K partials of the weight-gradient GEMMs
   long long splitk_floats;
   long long ce_rows;
+  long long* guard_tab;      // device copy of the guard offsets (first region, unguarded)
+  std::vector<long long> guard_offs;
 };
+
+// Guards: one per region, at most this many for a config (per layer 11 regions, ~30 more).
+long long guard_capacity(const gpt_config& c) { return 64 + 16LL * c.n_layer; }
 
 Plan carve_plan(const gpt_config& c, Carver& cv) {
   Plan p;
   const long long N = (long long)c.batch * c.seq_len, D = c.d_model, F = c.d_mlp, H = c.n_head;
+  // the guard table comes first; every region after it is followed by a guard, so a kernel
+  // that writes past the end of its buffer overwrites a guard word (gpt_check_errors, bit 4)
+  p.guard_tab = cv.take<long long>(guard_capacity(c));
+  cv.guard = true;
   const size_t es = c.dtype == GPT_BF16 ? 2 : 4;
   auto T = [&](long long n) { return (void*)cv.take<char>(n * es); };
   const bool vadd = c.has_v_add || c.has_trigram;
@@ -153,6 +162,7 @@ Plan carve_plan(const gpt_config& c, Carver& cv) {
     for (long long x : need) p.splitk_floats = std::max(p.splitk_floats, x);
   }
   p.splitk = p.splitk_floats ? cv.take<float>(p.splitk_floats) : nullptr;
+  p.guard_offs.assign(cv.guards.begin(), cv.guards.end());
   return p;
 }
 
@@ -443,6 +453,15 @@ gpt_status gpt_init(const gpt_config* cfg, void* workspace, size_t ws_bytes, hip
     st = launch_rope_table<float>((float*)plan.cos_t, (float*)plan.sin_t, cfg->seq_len,
                                   cfg->head_dim, cfg->rope_base, stream);
   if (st == GPT_OK) st = launch_fill((float*)plan.n_valid, 64, 0.f, stream);
+  if (st == GPT_OK) {
+    // the guard table (the context keeps the host copy alive for the asynchronous copy)
+    const int ng = (int)ctx->plan.guard_offs.size();
+    if (ng > guard_capacity(*cfg)) st = fail(GPT_ESHAPE, "gpt_init: too many workspace regions");
+    else if (hipMemcpyAsync(ctx->plan.guard_tab, ctx->plan.guard_offs.data(), ng * sizeof(long long),
+                            hipMemcpyHostToDevice, stream) != hipSuccess)
+      st = fail(GPT_EHIP, "gpt_init: guard table copy failed");
+    else st = launch_guards((char*)workspace, ctx->plan.guard_tab, ng, nullptr, 0, stream);
+  }
   if (st != GPT_OK) {
     delete ctx;
     return st;
@@ -477,6 +496,9 @@ gpt_status gpt_fwd_bwd(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targe
 
 gpt_status gpt_check_errors(gpt_ctx* ctx, hipStream_t stream, int32_t* flags) {
   if (!ctx || !flags) return fail(GPT_EINVAL, "gpt_check_errors: null argument");
+  gpt_status gs = launch_guards((char*)ctx->ws, ctx->plan.guard_tab,
+                                (int)ctx->plan.guard_offs.size(), ctx->plan.err, 1, stream);
+  if (gs != GPT_OK) return gs;
   int32_t h = 0;
   if (hipMemcpyAsync(&h, ctx->plan.err, sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess)

@@ -122,8 +122,10 @@ gpt_status gpt_fwd_bwd(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targe
                        void* d_x0_add, void* d_v_add, float* loss, hipStream_t stream);
 
 /* Bit flags of problems the kernels of this context detected since the last call:
- * 1 = an input token id outside [0, vocab); 2 = a target id outside [-1, vocab).  The
- * offending ids were clamped (inputs) or ignored (targets), so nothing faulted.
+ * 1 = an input token id outside [0, vocab); 2 = a target id outside [-1, vocab) (the offending
+ * ids were clamped or ignored, so nothing faulted); 4 = a guard region of the workspace was
+ * overwritten: every buffer gpt_init carves is followed by 256 guard bytes holding a known
+ * pattern, checked here, so a kernel writing past the end of its buffer is reported.
  * Synchronises `stream`, then clears the flags.  flags [host]. */
 gpt_status gpt_check_errors(gpt_ctx* ctx, hipStream_t stream, int32_t* flags);
 

@@ -81,6 +81,7 @@ def test_speedrun_accumulated_step_with_table_updates():
     B.bigram_bwd_update(h_x0, slab_x0, tx0, vx0, tc.lr)
     B.bigram_bwd_update(h_v, slab_v, tv, vv, tc.lr)
     torch.cuda.synchronize()
+    assert B.gpt_check_errors(ctx) == 0             # no kernel wrote past its buffer
 
     # ---- oracle: the kept sequences, their addends rebuilt from the same (initial) tables
     want_g = None

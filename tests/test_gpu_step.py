@@ -136,6 +136,24 @@ def test_step_is_bitwise_deterministic():
     assert torch.equal(g1, step.grads) and torch.equal(d1, step.d_v)
 
 
+def test_workspace_guards_report_an_overwrite():
+    """Every buffer of the step's workspace is followed by 256 guard bytes; after a step they are
+    intact, and a byte changed in the last guard (the workspace's final 256 bytes) is reported as
+    bit 4 by gpt_check_errors, then cleared."""
+    cfg, params, tok, x0, va, tri = _tiny(True, True)
+    step = Step(cfg, params)
+    step.run(tok, tok[:, 1:], x0, va, tri)
+    assert B.gpt_check_errors(step.ctx) == 0
+    n = B.gpt_workspace_bytes(cfg)
+    ws = step.ctx.workspace
+    ws[n - 3] = ws[n - 3] ^ 0x40                   # inside the last guard region
+    torch.cuda.synchronize()
+    assert B.gpt_check_errors(step.ctx) == 4
+    ws[n - 3] = ws[n - 3] ^ 0x40
+    torch.cuda.synchronize()
+    assert B.gpt_check_errors(step.ctx) == 0
+
+
 def test_out_of_range_ids_are_flagged_not_faulting():
     cfg, params, tok, _, _, _ = _tiny(False, False)
     step = Step(cfg, params)
@@ -169,6 +187,7 @@ def test_gpt2_small_bf16_full_launch_sampled_sequences():
     sub = cfg.replace(batch=len(keep))
     res = om.forward_backward(sub, params, tok[keep])
     _compare(cfg, res, step, loss, 1e-2, 3e-2, cos_min=0.999)
+    assert B.gpt_check_errors(step.ctx) == 0        # no kernel wrote past its buffer
 
 
 @pytest.mark.timeout(900)
@@ -190,6 +209,7 @@ def test_d32_bf16_full_launch_one_full_sequence():
     B.gpt_fwd_bwd(ctx, dev(np.ascontiguousarray(tok[:, :T]).astype(np.int32)), dev(tgt), flat,
                   grads, loss_t, 1.0, 0, None, None, None, None, None)
     torch.cuda.synchronize()
+    assert B.gpt_check_errors(ctx) == 0             # no kernel wrote past its buffer
     loss = float(loss_t.item())
     got = inputs.unflatten(cfg, host(grads))
     del grads
