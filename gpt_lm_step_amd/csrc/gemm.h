@@ -1099,12 +1099,26 @@ void launch_tiles(bool a_kc, bool b_kc, int M, int N, int K, const T* A, long lo
 
 }  // namespace gemm_detail
 
+namespace gemm_detail {
+// Tile size of a bf16 product from the quantisation of its output tiling.  A 256 x 256 tile
+// (one workgroup per CU) does about 1.25x the work per CU-cycle of two co-resident 128 x 128
+// tiles (measured at K = 768 and 2048), but with 256 tiles per round a last, partly filled round
+// can leave most CUs idle (GPT-2-small's 8192 x 2304 q/k/v projection: 288 tiles, two rounds,
+// 56% busy; as 128 x 128 tiles, 1152 over 512 slots, 75%).  Whichever tiling keeps more of the
+// chip's slots busy, weighted by that factor, is used.
+inline bool prefer_big_tiles(long long tiles256, long long tiles128) {
+  auto busy = [](long long t, long long slots) {
+    return (double)t / (double)(slots * ((t + slots - 1) / slots));
+  };
+  return 1.25 * busy(tiles256, 256) >= busy(tiles128, 512);
+}
+}  // namespace gemm_detail
+
 // C[m,n] = sum_k A(m,k) B(n,k); a_kc/b_kc select K-contiguous (p[r*ld+k]) or row-contiguous
 // (p[k*ld+r]) operands.  Requirements: K % 8 == 0, lda/ldb % 8 == 0, 16-byte aligned operands,
 // M % 8 == 0 for a row-contiguous A, N % 8 == 0 for a row-contiguous B, N % 4 == 0 and output
-// leading dimensions (inside the epilogue) multiples of 4.  bf16 problems whose
-// 256 x 256 tiling fills the GPU (>= 240 tiles for 256 CUs) use that tile, the rest 128 x 128;
-// fp32 uses 64 x 64.
+// leading dimensions (inside the epilogue) multiples of 4.  bf16 problems use 256 x 256 or
+// 128 x 128 tiles as prefer_big_tiles decides; fp32 uses 64 x 64.
 template <int SITE, typename T, class Epi>
 inline gpt_status gemm(bool a_kc, bool b_kc, int M, int N, int K, const T* A, long long lda,
                        const T* B, long long ldb, const Epi& epi, hipStream_t s) {
@@ -1120,18 +1134,19 @@ inline gpt_status gemm(bool a_kc, bool b_kc, int M, int N, int K, const T* A, lo
     return fail(GPT_ESHAPE, "gemm: each operand must span at most 2 GiB");
   if (epi_wave_cols<Epi>::value != 64 && (!a_kc || !b_kc || !std::is_same<T, bf16>::value))
     return fail(GPT_EINVAL, "gemm: this epilogue needs bf16 K-contiguous operands");
-  const long long big_tiles = (long long)cdiv(M, 256) * cdiv(N, 256);
   if ((long long)cdiv(M, 128) * cdiv(N, 128) >= (1LL << 31)) return fail(GPT_ESHAPE, "gemm: too many tiles");
+  const bool big = gemm_detail::prefer_big_tiles((long long)cdiv(M, 256) * cdiv(N, 256),
+                                                 (long long)cdiv(M, 128) * cdiv(N, 128));
   gemm_detail::with_static_epi(epi, [&](const auto& e) {
     using E = typename std::decay<decltype(e)>::type;
     if constexpr (std::is_same<T, bf16>::value) {
       if constexpr (epi_wave_cols<E>::value == 128) {
         // wave tiles of 64 x 128 (4 x 2 waves) or 32 x 128 (4 x 1)
-        if (big_tiles >= 240)
+        if (big)
           gemm_detail::launch_dma<256, 256, 4, 2, E, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, e, s);
         else
           gemm_detail::launch_dma<128, 128, 4, 1, E, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, e, s);
-      } else if (big_tiles >= 240) {
+      } else if (big) {
         gemm_detail::launch_dma<256, 256, 2, 4, E, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, e, s);
       } else {
         gemm_detail::launch_dma<128, 128, 2, 2, E, SITE>(a_kc, b_kc, M, N, K, A, lda, B, ldb, e, s);
