@@ -1195,14 +1195,33 @@ inline gpt_status gemm_batched(bool a_kc, bool b_kc, int M, int N, int K, const 
 namespace gemm_detail {
 
 // Split-K for bf16 GEMMs with an fp32 output (weight gradients) whose output tiling alone leaves
-// CUs idle: prefer 256 x 256 tiles with 2..8 splits of >= 1024 K each when that gives >= 480
-// workgroups (about two per CU), else 128 x 128 tiles (two workgroups per CU) with up to 16
-// splits of >= 512 K.  A function of the shape only, so workspace sizing and launch agree.
+// CUs idle.  The shapes of the shipped workloads take the plan measured best on MI355X (a sweep
+// of tile size x 1..16 splits, GEMM plus reduction, same box); other shapes: 256 x 256 tiles with
+// 2..8 splits of >= 1024 K each when that gives >= 480 workgroups (about two per CU), else
+// 128 x 128 tiles (two workgroups per CU) with up to 16 splits of >= 512 K.  A function of the
+// shape only, so workspace sizing and launch agree.
 struct SplitPlan {
   int splits;
   bool big;
 };
+struct TunedSplit {
+  int M, N, K;
+  SplitPlan plan;
+};
+// (µs per product on the sweep's box: best plan vs the general rule's)
+constexpr TunedSplit kTunedSplits[] = {
+    // GPT-2-small weight gradients over 8,192 tokens (also the speedrun micro-batches)
+    {3072, 768, 8192, {2, false}},   // MLP up:   61.7 vs 63.6-73.4 (128 x 128, 4 splits)
+    {768, 3072, 8192, {2, false}},   // MLP down: 58.9 vs 63.0-63.7
+    {2304, 768, 8192, {4, false}},   // q/k/v:    40.0 vs 50.9-51.0 (8 splits)
+    {768, 768, 8192, {4, false}},    // out, trigram projection: 26.6 vs 39.9 (16 splits)
+    // d32 weight gradients over 16,384 tokens
+    {2048, 2048, 16384, {4, true}},  // out:   132-134 vs 160-162 (256 x 256, 8 splits)
+    {6144, 2048, 16384, {1, true}},  // q/k/v: 350-354 vs 394-396 (256 x 256, 4 splits)
+};
 inline SplitPlan split_plan(int M, int N, int K) {
+  for (const TunedSplit& t : kTunedSplits)
+    if (t.M == M && t.N == N && t.K == K) return t.plan;
   const long long t256 = (long long)cdiv(M, 256) * cdiv(N, 256);
   if (t256 >= 240) return {1, true};
   for (int sp = 2; sp <= 8; sp *= 2)

@@ -309,20 +309,20 @@ struct FinishIn {
   typename Raw4<S>::type raw[G];  // MODE_UPDATE: table row; MODE_GRAD: old output row
   float v;                        // MODE_UPDATE: second moment of the row
   bool have;                      // MODE_GRAD: beta = 1 (old output row loaded)
-  __device__ __forceinline__ void fetch(const Finish<T>& f, uint32_t row, int dim) {
+  __device__ __forceinline__ void fetch(const Finish<T>& f, uint32_t row, int stride, int width) {
     const S* p;
     if constexpr (MODE == MODE_UPDATE) {
       v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(row_rsrc(f.v + row, 4), 0, 0, 0));
-      p = f.table + (size_t)row * dim;
+      p = f.table + (size_t)row * stride;
       have = true;
     } else {
       v = 0.f;
-      p = f.out + (size_t)row * dim;
+      p = f.out + (size_t)row * stride;
       have = f.beta != 0;
     }
-    const __amdgpu_buffer_rsrc_t rs = row_rsrc(p, dim * (int)sizeof(S));
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(p, width * (int)sizeof(S));
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi) raw[gi] = Raw4<S>::load(rs, have ? group_off(gi, dim) : ROW_OOB / 4);
+    for (int gi = 0; gi < G; ++gi) raw[gi] = Raw4<S>::load(rs, have ? group_off(gi, width) : ROW_OOB / 4);
   }
   __device__ __forceinline__ void values(float (&w)[G][4]) const {
 #pragma unroll
@@ -332,8 +332,10 @@ struct FinishIn {
 
 // MODE_UPDATE: v = beta2 v + (1 - beta2) mean(g^2); w -= lr g / (sqrt(v) + eps).
 // MODE_GRAD: out = (beta ? out : 0) + g.
+// Row `row` of `stride` elements, of which this wave owns `width` (MODE_UPDATE: the whole row,
+// since its statistic needs every element; MODE_GRAD: one column slice, pointers pre-offset).
 template <typename T, int MODE, int G>
-__device__ __forceinline__ void finish_row(const Finish<T>& f, uint32_t row, int dim,
+__device__ __forceinline__ void finish_row(const Finish<T>& f, uint32_t row, int stride, int width,
                                            const float (&acc)[G][4], const FinishIn<T, MODE, G>& in) {
   float w[G][4];
   in.values(w);
@@ -342,8 +344,9 @@ __device__ __forceinline__ void finish_row(const Finish<T>& f, uint32_t row, int
     for (int gi = 0; gi < G; ++gi)
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[gi][e] += acc[gi][e];
-    store_row<G>(f.out + (size_t)row * dim, dim, w);
+    store_row<G>(f.out + (size_t)row * stride, width, w);
   } else {
+    const int dim = width;
     float ss = 0.f;
 #pragma unroll
     for (int gi = 0; gi < G; ++gi)
@@ -356,7 +359,7 @@ __device__ __forceinline__ void finish_row(const Finish<T>& f, uint32_t row, int
     for (int gi = 0; gi < G; ++gi)
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[gi][e] -= step * acc[gi][e];
-    store_row<G>(f.table + (size_t)row * dim, dim, w);
+    store_row<G>(f.table + (size_t)row * stride, dim, w);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(vr), row_rsrc(f.v + row, 4),
                                           threadIdx.x % WAVE == 0 ? 0u : ROW_OOB, 0, 0);
   }
@@ -371,15 +374,15 @@ constexpr uint32_t NO_KEY = 0xffffffffu;  // above every key (keys <= rows < 2^3
 // lane-indexed), in ascending order with U rows in flight.  Slots past pe load zeros, which
 // leave the sum unchanged, so the U loads of a round are issued back to back.
 template <int G, int U, typename DyT>
-__device__ __forceinline__ void sum_rows(const DyT* __restrict__ dy, int dim, uint32_t tok, int j,
-                                         int pe, float (&acc)[G][4]) {
+__device__ __forceinline__ void sum_rows(const DyT* __restrict__ dy, int stride, int width,
+                                         uint32_t tok, int j, int pe, float (&acc)[G][4]) {
   zero_acc<G>(acc);
   for (int j0 = j; j0 < pe; j0 += U) {
     float x[U][G][4];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const size_t t = (uint32_t)__builtin_amdgcn_readlane((int)tok, min(j0 + u, pe - 1));
-      load_row<G>(dy + t * dim, dim, x[u], j0 + u < pe);
+      load_row<G>(dy + t * stride, width, x[u], j0 + u < pe);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -403,22 +406,22 @@ template <typename T, typename DyT, int MODE, int G, int U>
 struct PieceLoads {
   FinishIn<T, MODE, G> in;
   typename Raw4<DyT>::type x[U][G];
-  __device__ __forceinline__ void issue(const Piece& p, const DyT* __restrict__ dy, int dim,
-                                        uint32_t tok, const Finish<T>& fin) {
-    in.fetch(fin, p.live ? p.row : 0u, dim);
+  __device__ __forceinline__ void issue(const Piece& p, const DyT* __restrict__ dy, int stride,
+                                        int width, uint32_t tok, const Finish<T>& fin) {
+    in.fetch(fin, p.live ? p.row : 0u, stride, width);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool on = p.live && p.j + u < p.pe;
       const size_t t = (uint32_t)__builtin_amdgcn_readlane((int)tok, min(p.j + u, p.pe - 1));
-      const DyT* r = dy + t * dim;
-      const __amdgpu_buffer_rsrc_t rs = row_rsrc(r, dim * (int)sizeof(DyT));
+      const DyT* r = dy + t * stride;
+      const __amdgpu_buffer_rsrc_t rs = row_rsrc(r, width * (int)sizeof(DyT));
 #pragma unroll
-      for (int gi = 0; gi < G; ++gi) x[u][gi] = Raw4<DyT>::load(rs, on ? group_off(gi, dim) : ROW_OOB / 4);
+      for (int gi = 0; gi < G; ++gi) x[u][gi] = Raw4<DyT>::load(rs, on ? group_off(gi, width) : ROW_OOB / 4);
     }
   }
   // the piece's gradient sum: the rows in flight, then (long pieces) the rest
-  __device__ __forceinline__ void sum(const Piece& p, const DyT* __restrict__ dy, int dim,
-                                      uint32_t tok, float (&acc)[G][4]) const {
+  __device__ __forceinline__ void sum(const Piece& p, const DyT* __restrict__ dy, int stride,
+                                      int width, uint32_t tok, float (&acc)[G][4]) const {
     zero_acc<G>(acc);
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -431,7 +434,7 @@ struct PieceLoads {
       }
     if (p.j + U < p.pe) {
       float rest[G][4];
-      sum_rows<G, U>(dy, dim, tok, p.j + U, p.pe, rest);
+      sum_rows<G, U>(dy, stride, width, tok, p.j + U, p.pe, rest);
 #pragma unroll
       for (int gi = 0; gi < G; ++gi)
 #pragma unroll
@@ -447,12 +450,19 @@ struct PieceLoads {
 // 2*tile + 1.  Keys past the table (the sentinel) form a suffix and are skipped.  The complete
 // pieces are finished in a loop whose every pass issues the loads of the next piece, stores
 // the current one and then consumes the next piece's loads, so no load wait covers a store.
+// Rows have `stride` elements; blockIdx.y selects the column slice [y * sw, y * sw + sw) that
+// the block's waves own (MODE_GRAD splits wide rows so that small n still fills the GPU;
+// MODE_UPDATE has one slice, sw = stride, as its row statistic needs the whole row).
 template <typename T, typename DyT, int MODE, int G>
 __global__ __launch_bounds__(256) void seg_tile_kernel(
     const uint32_t* __restrict__ skeys, const uint32_t* __restrict__ svals,
-    const DyT* __restrict__ dy, long long n, int dim, long long rows,
+    const DyT* __restrict__ dy, long long n, int stride, int sw, long long rows,
     float* __restrict__ partial, Finish<T> fin) {
   constexpr int U = unroll_rows<G>();
+  const int col0 = blockIdx.y * sw, width = min(sw, stride - col0);
+  dy += col0;
+  partial += col0;
+  if constexpr (MODE == MODE_GRAD) fin.out += col0;
   const int lane = threadIdx.x % WAVE;
   const int wpb = blockDim.x / WAVE;
   const long long ntiles = (n + SEG_TILE - 1) / SEG_TILE;
@@ -482,8 +492,8 @@ __global__ __launch_bounds__(256) void seg_tile_kernel(
     };
     auto to_partial = [&](const Piece& p, long long slot) {
       float acc[G][4];
-      sum_rows<G, U>(dy, dim, tok, p.j, p.pe, acc);
-      store_row<G>(partial + (size_t)slot * dim, dim, acc);
+      sum_rows<G, U>(dy, stride, width, tok, p.j, p.pe, acc);
+      store_row<G>(partial + (size_t)slot * stride, width, acc);
     };
     if (lim == 0) continue;
     int a = 0, b = lim;  // the complete pieces cover positions [a, b)
@@ -510,20 +520,20 @@ __global__ __launch_bounds__(256) void seg_tile_kernel(
     };
     Piece cur = clip(piece_at(a));
     PieceLoads<T, DyT, MODE, G, U> ld;
-    ld.issue(cur, dy, dim, tok, fin);
+    ld.issue(cur, dy, stride, width, tok, fin);
     float acc[G][4];
-    ld.sum(cur, dy, dim, tok, acc);
+    ld.sum(cur, dy, stride, width, tok, acc);
     FinishIn<T, MODE, G> in = ld.in;
     while (true) {
       // past the last piece the next one is not live: it loads and sums zeros
       const Piece nxt = clip(piece_at(min(cur.pe, WAVE - 1)));
-      ld.issue(nxt, dy, dim, tok, fin);
+      ld.issue(nxt, dy, stride, width, tok, fin);
       __builtin_amdgcn_sched_barrier(0);  // the next piece's loads stay ahead of these stores
-      finish_row<T, MODE, G>(fin, cur.row, dim, acc, in);
+      finish_row<T, MODE, G>(fin, cur.row, stride, width, acc, in);
       __builtin_amdgcn_sched_barrier(0);
       const bool last = cur.pe >= b;
       cur = nxt;
-      ld.sum(cur, dy, dim, tok, acc);
+      ld.sum(cur, dy, stride, width, tok, acc);
       in = ld.in;
       if (last) break;
     }
@@ -532,12 +542,16 @@ __global__ __launch_bounds__(256) void seg_tile_kernel(
 
 // One wavefront per row that starts in a tile and goes on past it (found at that tile): adds
 // the row's first partial and then the partials of the following tiles, which begin with the
-// row, in tile order.  Their first keys are read 64 tiles at a time.
+// row, in tile order.  Their first keys are read 64 tiles at a time.  Column slices as in
+// seg_tile_kernel.
 template <typename T, int MODE, int G>
 __global__ __launch_bounds__(256) void seg_tile_finish_kernel(
-    const uint32_t* __restrict__ skeys, long long n, int dim, long long rows,
+    const uint32_t* __restrict__ skeys, long long n, int stride, int sw, long long rows,
     const float* __restrict__ partial, Finish<T> fin) {
   constexpr int U = G <= 4 ? 8 : 4;  // partial rows in flight
+  const int col0 = blockIdx.y * sw, width = min(sw, stride - col0);
+  partial += col0;
+  if constexpr (MODE == MODE_GRAD) fin.out += col0;
   const int lane = threadIdx.x % WAVE;
   const int wpb = blockDim.x / WAVE;
   const long long ntiles = (n + SEG_TILE - 1) / SEG_TILE;
@@ -549,9 +563,9 @@ __global__ __launch_bounds__(256) void seg_tile_finish_kernel(
     if (row >= rows || skeys[P + SEG_TILE] != row) continue;         // last piece ends here
     if (skeys[P] == row && P > 0 && skeys[P - 1] == row) continue;    // the row began earlier
     FinishIn<T, MODE, G> in;
-    in.fetch(fin, row, dim);
+    in.fetch(fin, row, stride, width);
     float acc[G][4];
-    load_row<G>(partial + (size_t)(2 * tile + 1) * dim, dim, acc);
+    load_row<G>(partial + (size_t)(2 * tile + 1) * stride, width, acc);
     for (long long t0 = tile + 1;; t0 += WAVE) {
       const long long t = t0 + lane;
       const bool cont = t < ntiles && skeys[t * SEG_TILE] == row;  // a prefix of the lanes
@@ -560,7 +574,7 @@ __global__ __launch_bounds__(256) void seg_tile_finish_kernel(
         float x[U][G][4];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          load_row<G>(partial + (size_t)(2 * (t0 + min(j0 + u, cnt - 1))) * dim, dim, x[u],
+          load_row<G>(partial + (size_t)(2 * (t0 + min(j0 + u, cnt - 1))) * stride, width, x[u],
                       j0 + u < cnt);
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -571,7 +585,7 @@ __global__ __launch_bounds__(256) void seg_tile_finish_kernel(
       }
       if (cnt < WAVE) break;
     }
-    finish_row<T, MODE, G>(fin, row, dim, acc, in);
+    finish_row<T, MODE, G>(fin, row, stride, width, acc, in);
   }
 }
 
@@ -622,13 +636,20 @@ gpt_status segsum_run(const int32_t* keys, const DyT* dy, long long n, int dim, 
   }
 
   const long long ntiles = (n + SEG_TILE - 1) / SEG_TILE;
+  // MODE_GRAD: rows wider than 256 elements are split into 256-wide column slices while the
+  // tiles alone give fewer than 2048 wavefronts (the embedding gradient of 16,384 tokens has
+  // 256 tiles: 8 slices of a 2048-wide row give 2048 wavefronts with 8 rows in flight each)
+  int sw = dim;
+  if (MODE == MODE_GRAD)
+    while (sw > 256 && ntiles * cdiv(dim, sw) < 2048) sw = (int)(cdiv(sw / 2, 4) * 4);
   const unsigned grid = (unsigned)std::min<long long>(cdiv(ntiles, 4), 16384);
-  const int g4 = (dim / 4 + WAVE - 1) / WAVE;
-#define SEG_LAUNCH(G)                                                                           \
-  do {                                                                                          \
-    seg_tile_kernel<T, DyT, MODE, G><<<grid, 256, 0, s>>>(ki, vi, dy, n, dim, rows, w.partial,  \
-                                                          fin);                                 \
-    seg_tile_finish_kernel<T, MODE, G><<<grid, 256, 0, s>>>(ki, n, dim, rows, w.partial, fin);  \
+  const dim3 g2(grid, (unsigned)cdiv(dim, sw));
+  const int g4 = (sw / 4 + WAVE - 1) / WAVE;
+#define SEG_LAUNCH(G)                                                                             \
+  do {                                                                                            \
+    seg_tile_kernel<T, DyT, MODE, G><<<g2, 256, 0, s>>>(ki, vi, dy, n, dim, sw, rows, w.partial,  \
+                                                        fin);                                     \
+    seg_tile_finish_kernel<T, MODE, G><<<g2, 256, 0, s>>>(ki, n, dim, sw, rows, w.partial, fin);  \
   } while (0)
   switch (g4) {
     case 1: SEG_LAUNCH(1); break;

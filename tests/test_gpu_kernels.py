@@ -66,9 +66,11 @@ def test_gemm_large_square_bf16():
 
 
 @pytest.mark.parametrize("a_kc,b_kc,M,N,K,splits", [
-    (0, 0, 768, 768, 8192, 16),     # 128-tile plan, 16 splits (GPT-2-small output projection)
-    (0, 0, 2304, 768, 8192, 8),     # 128-tile plan, 8 splits
-    (0, 0, 2048, 2048, 16384, 8),   # 256-tile plan, 8 splits
+    (0, 0, 768, 768, 8192, 4),      # measured plan: 128 tiles, 4 splits (GPT-2-small out proj.)
+    (0, 0, 2304, 768, 8192, 4),     # measured plan: 128 tiles, 4 splits (GPT-2-small q/k/v)
+    (0, 0, 2048, 2048, 16384, 4),   # measured plan: 256 tiles, 4 splits (d32 out proj.)
+    (0, 0, 640, 640, 8192, 16),     # general rule: 128 tiles, 16 splits
+    (0, 0, 2560, 1536, 16384, 8),   # general rule: 256 tiles, 8 splits
     (1, 0, 392, 520, 4104, 8),      # ragged M, N and a last split shorter than the others
     (0, 1, 264, 136, 2056, 4),
     (1, 1, 256, 384, 128, 1),       # too short to split
