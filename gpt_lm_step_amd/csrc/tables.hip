@@ -119,15 +119,36 @@ __global__ void radix_hist(const int32_t* __restrict__ h, const uint32_t* __rest
 
 // Scatter offset of digit d in tile blk: all keys of smaller digits plus digit d's keys in
 // earlier tiles (exclusive scan of hist in [digit][tile] order).
+// The digit's row of tile counts is read 64 counts per round trip (16-byte loads, all issued
+// before any is used) when its length allows it.
 __device__ __forceinline__ int digit_offset(const int* __restrict__ hist, int nblk, int* smem) {
   const int d = threadIdx.x;
   const int* row = hist + (long long)d * nblk;
+  const int me = (int)blockIdx.x;
   int before = 0, total = 0;
+  if (nblk % 4 == 0) {  // rows of 16-byte groups (the workspace is 256-byte aligned)
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const i32x4* row4 = reinterpret_cast<const i32x4*>(row);
+    const int n4 = nblk / 4;
+    for (int c0 = 0; c0 < n4; c0 += 16) {
+      i32x4 v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = c0 + i < n4 ? row4[c0 + i] : i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          total += v[i][e];
+          before += 4 * (c0 + i) + e < me ? v[i][e] : 0;
+        }
+    }
+  } else {
 #pragma unroll 8
-  for (int b = 0; b < nblk; ++b) {
-    const int c = row[b];
-    total += c;
-    before += (b < (int)blockIdx.x) ? c : 0;
+    for (int b = 0; b < nblk; ++b) {
+      const int c = row[b];
+      total += c;
+      before += (b < me) ? c : 0;
+    }
   }
   int all;
   return block_excl_scan(total, smem, &all) + before;
@@ -164,25 +185,35 @@ __global__ void radix_scatter(const int32_t* __restrict__ h, long long rows,
   __shared__ int wcnt[RS_THREADS / WAVE][256];
   __shared__ int smem[16];
   const int tid = threadIdx.x, lane = tid % WAVE, w = tid / WAVE;
+  // every round's key and value are loaded up front (one memory round trip for the tile, in
+  // flight while the digit offsets are formed)
+  uint32_t kr[RS_ROUNDS], vr[RS_ROUNDS];
+#pragma unroll
+  for (int r = 0; r < RS_ROUNDS; ++r) {
+    const long long i = (long long)blockIdx.x * RS_TILE + r * RS_THREADS + tid;
+    kr[r] = 0;
+    vr[r] = 0;
+    if (i < n) {
+      if (h) {
+        kr[r] = clamp_key(h[i], rows);
+        vr[r] = (uint32_t)i;
+      } else {
+        kr[r] = kin[i];
+        vr[r] = vin[i];
+      }
+    }
+  }
   base[tid] = scanned ? hist[(long long)tid * nblk + blockIdx.x] : digit_offset(hist, nblk, smem);
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
   for (int r = 0; r < RS_ROUNDS; ++r) {
 #pragma unroll
     for (int q = 0; q < RS_THREADS / WAVE; ++q) wcnt[q][tid] = 0;
     __syncthreads();
     const long long i = (long long)blockIdx.x * RS_TILE + r * RS_THREADS + tid;
     const bool valid = i < n;
-    uint32_t k = 0, v = 0, d = 0;
-    if (valid) {
-      if (h) {
-        k = clamp_key(h[i], rows);
-        v = (uint32_t)i;
-      } else {
-        k = kin[i];
-        v = vin[i];
-      }
-      d = (k >> shift) & 255u;
-    }
+    const uint32_t k = kr[r], v = vr[r];
+    const uint32_t d = valid ? (k >> shift) & 255u : 0u;
     uint64_t mask = __ballot(valid);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
