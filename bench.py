@@ -57,15 +57,18 @@ def multi_stages(B, cfg):
 
 # Kernels whose HBM traffic has been measured with rocprofv3 counters (profiles/traffic.json): the
 # stage name, substrings of the kernel symbol ('|'-separated alternatives: mangled or demangled)
-# that identify it in the counter output, and the source file the measurement belongs to.
+# that identify it in the counter output, the source file the measurement belongs to, and the
+# workloads whose runs measure it (a symbol pattern names that stage's kernel only there: the
+# decode workload's prefill launches the training GEMMs too).
+TRAINING = ("d32", "gpt2", "speedrun")
 TRAFFIC_KERNELS = {
-    "down_dgrad": ("EpiDRelu2", "gemm.h"),
-    "up_fwd": ("EpiRelu2", "gemm.h"),
-    "down_fwd": ("EpiResidELi4E|EpiResid, 4>", "gemm.h"),
-    "attn_bwd_dkdv": ("attn_bwd_dkdv_pipe_kernel", "attn.hip"),
-    "softcap_ce": ("9ce_kernelI|::ce_kernel<", "ce.hip"),
-    "bigram_fwd (hash + gather-add, x0 table)": ("bigram_gather_kernel", "tables.hip"),
-    "attn_split": ("attn_split_kernel", "infer.hip"),
+    "down_dgrad": ("EpiDRelu2", "gemm.h", TRAINING),
+    "up_fwd": ("EpiRelu2", "gemm.h", TRAINING),
+    "down_fwd": ("EpiResidELi4E|EpiResid, 4>", "gemm.h", TRAINING),
+    "attn_bwd_dkdv": ("attn_bwd_dkdv_pipe_kernel", "attn.hip", TRAINING),
+    "softcap_ce": ("9ce_kernelI|::ce_kernel<", "ce.hip", TRAINING),
+    "bigram_fwd (hash + gather-add, x0 table)": ("bigram_gather_kernel", "tables.hip", ("tables",)),
+    "attn_split": ("attn_split_kernel", "infer.hip", ("decode",)),
 }
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gpt_lm_step_amd", "csrc")
@@ -117,7 +120,9 @@ def record_traffic(a):
         entries = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         entries = []
-    for stage, (pattern, source) in TRAFFIC_KERNELS.items():
+    for stage, (pattern, source, workloads) in TRAFFIC_KERNELS.items():
+        if a.workload not in workloads:
+            continue
         try:
             fk = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", pattern)
             wk = _counter_per_dispatch(write_dir, "WRITE_SIZE", pattern)
