@@ -667,12 +667,14 @@ gpt_status segsum_run(const int32_t* keys, const DyT* dy, long long n, int dim, 
   }
 
   const long long ntiles = (n + SEG_TILE - 1) / SEG_TILE;
-  // MODE_GRAD: rows wider than 256 elements are split into 256-wide column slices while the
-  // tiles alone give fewer than 2048 wavefronts (the embedding gradient of 16,384 tokens has
-  // 256 tiles: 8 slices of a 2048-wide row give 2048 wavefronts with 8 rows in flight each)
+  // MODE_GRAD: rows of a multiple of 512 elements are halved into column slices (of at least
+  // 256, so every lane of a wave has work) while the tiles alone give fewer than 2048 wavefronts
+  // (the embedding gradient of 16,384 tokens has 256 tiles: 8 slices of a 2048-wide row give
+  // 2048 wavefronts with 8 rows in flight each).  A 768-wide row stays whole: its 192-wide
+  // quarters left a quarter of the lanes idle and ran slower (GPT-2-small: 45.6 -> 54 us).
   int sw = dim;
   if (MODE == MODE_GRAD)
-    while (sw > 256 && ntiles * cdiv(dim, sw) < 2048) sw = (int)(cdiv(sw / 2, 4) * 4);
+    while (sw % 512 == 0 && ntiles * (dim / sw) < 2048) sw /= 2;
   const unsigned grid = (unsigned)std::min<long long>(cdiv(ntiles, 4), 16384);
   const dim3 g2(grid, (unsigned)cdiv(dim, sw));
   const int g4 = (sw / 4 + WAVE - 1) / WAVE;
