@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -32,7 +33,7 @@ PEAK_FP32 = 157.3e12     # MI355X fp32 (matrix and vector), FLOP/s
 PEAK_HBM = 8.0e12        # MI355X HBM3E, B/s
 METRIC = "train tokens/sec (fwd+bwd) on 1 MI355X + MFU vs bf16 MFMA peak"
 DENSE = {"d32": configs.D32, "gpt2": configs.GPT2_SMALL, "tiny": configs.TINY}
-WORKLOADS = sorted(list(DENSE) + ["tables", "speedrun", "copy", "opt", "decode"])
+WORKLOADS = sorted(list(DENSE) + ["tables", "speedrun", "copy", "opt", "decode", "gemm_ref"])
 # Stages made of several kernels (their time is not one kernel's launch duration); the weight-
 # gradient stages join them when their shape is split over K (see split_stages).
 MULTI_KERNEL = {"wte_segsum"}
@@ -160,6 +161,64 @@ def bench_copy(a):
     return {"metric": "device copy bytes/s (counter calibration)", "value": 2 * COPY_BYTES / ms / 1e6,
             "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
             "higher_is_better": True, "config": {"workload": "copy", "bytes": COPY_BYTES}}
+
+
+GEMM_REF_SHAPES = [  # (name, M, N, K): the step's forward products (tokens x out x in)
+    ("d32 q/k/v", 16384, 6144, 2048), ("d32 out", 16384, 2048, 2048),
+    ("d32 MLP up", 16384, 8192, 2048), ("d32 MLP down", 16384, 2048, 8192),
+    ("d32 LM head", 16384, 65536, 2048),
+    ("GPT-2 q/k/v", 8192, 2304, 768), ("GPT-2 out", 8192, 768, 768),
+    ("GPT-2 MLP up", 8192, 3072, 768), ("GPT-2 MLP down", 8192, 768, 3072),
+    ("GPT-2 LM head", 8192, 50304, 768),
+]
+
+
+def bench_gemm_ref(a, B):
+    """Context for the GEMM figures: this library's bf16 product (gptk_gemm, fp32 output, tile
+    size by its own rule) and hipBLASLt through torch.mm (bf16 output) on the step's product
+    shapes, the same operand layouts (A [M, K] K-contiguous, B stored [K, N]), each timed with
+    events over a.steps launches after a.warmup.  value = geometric mean of the library's
+    rate over hipBLASLt's."""
+    import torch
+    rows, ratios = [], []
+    g = torch.Generator(device="cuda").manual_seed(7)
+    for name, M, N, K in GEMM_REF_SHAPES:
+        x = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        w = torch.randn(K, N, device="cuda", generator=g).to(torch.bfloat16)
+        c = torch.empty(M, N, device="cuda")
+
+        def ours():
+            B.gptk_gemm(1, 0, M, N, K, x, K, w, N, c, N)
+
+        def lib():
+            return torch.mm(x, w)
+
+        def timed(f):
+            for _ in range(a.warmup):
+                f()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(a.steps):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / a.steps
+        t_ours, t_lib = timed(ours), timed(lib)
+        fl = 2.0 * M * N * K
+        rows.append({"product": name, "M": M, "N": N, "K": K,
+                     "ours_ms": round(t_ours, 4), "ours_tflops": round(fl / t_ours / 1e9, 1),
+                     "hipblaslt_ms": round(t_lib, 4), "hipblaslt_tflops": round(fl / t_lib / 1e9, 1)})
+        ratios.append(t_lib / t_ours)
+        print(f"{name:16s} {M:6d} {N:6d} {K:5d}  ours {rows[-1]['ours_tflops']:7.1f} TFLOP/s  "
+              f"hipBLASLt {rows[-1]['hipblaslt_tflops']:7.1f} TFLOP/s", file=sys.stderr, flush=True)
+        del x, w, c
+        torch.cuda.empty_cache()
+    gm = math.exp(sum(math.log(r) for r in ratios) / len(ratios))
+    return {"metric": "bf16 GEMM rate relative to hipBLASLt (geometric mean over the step's products)",
+            "value": round(gm, 4), "unit": "ratio", "n_gpus": 1, "steps": a.steps,
+            "warmup": a.warmup, "higher_is_better": True, "dtype": "bf16",
+            "config": {"workload": "gemm_ref", "products": rows}}
 
 
 def parse():
@@ -763,6 +822,8 @@ def main():
         sys.exit(2)
     if a.workload == "copy":
         out = bench_copy(a)
+    elif a.workload == "gemm_ref":
+        out = bench_gemm_ref(a, B)
     elif a.workload == "tables":
         out = bench_tables(a, B)
     elif a.workload == "speedrun":
