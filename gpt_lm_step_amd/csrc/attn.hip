@@ -592,9 +592,11 @@ __device__ __forceinline__ void pipe_schedule() {
 // zeroes P and dS, so they add nothing, and the loop body has no branches (the two S/dP register
 // sets stay fixed).  The loop is unrolled by four so each slot's LDS offset is a constant folded
 // into the read instructions.  One barrier per tile: slot j+3 is written while j and j+1 are read.
-// Sequence length: a multiple of 64.
+// Sequence length: a multiple of 64.  Up to head size 64 the registers are capped for two
+// workgroups per CU (a few spilled values; GPT-2-small's shape 58 -> 47.5 us per layer), at 128
+// one workgroup per CU holds every accumulator in registers.
 template <int HD>
-__global__ __launch_bounds__(ATHREADS, 1) void attn_bwd_dkdv_pipe_kernel(
+__global__ __launch_bounds__(ATHREADS, HD <= 64 ? 2 : 1) void attn_bwd_dkdv_pipe_kernel(
     const bf16* __restrict__ qkv, const bf16* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ dq_sum, bf16* __restrict__ dqkv, int Tn, int H, float sl2,
     float scale) {
