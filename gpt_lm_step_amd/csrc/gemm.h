@@ -1105,8 +1105,10 @@ namespace gemm_detail {
 // tiles (measured at K = 768 and 2048), but with 256 tiles per round a last, partly filled round
 // can leave most CUs idle (GPT-2-small's 8192 x 2304 q/k/v projection: 288 tiles, two rounds,
 // 56% busy; as 128 x 128 tiles, 1152 over 512 slots, 75%).  Whichever tiling keeps more of the
-// chip's slots busy, weighted by that factor, is used.
+// chip's slots busy, weighted by that factor, is used; a product whose 128 x 128 tiles each get
+// a CU of their own takes them (a quarter of the work per CU, no round to fill).
 inline bool prefer_big_tiles(long long tiles256, long long tiles128) {
+  if (tiles128 <= 256) return false;
   auto busy = [](long long t, long long slots) {
     return (double)t / (double)(slots * ((t + slots - 1) / slots));
   };
