@@ -239,9 +239,10 @@ __device__ __forceinline__ void store_acc_rows(T* __restrict__ dst_row, const f3
 // ------------------------------------------------------------------ forward
 // Workgroup: NWV waves x 32 queries.  K/V tiles of 64 keys are double buffered in LDS: each
 // iteration writes tile j+1 (held in registers) and loads tile j+2 before multiplying tile j.
-// bf16 (NWV = 8, two waves per SIMD): K and V as swizzled row tiles (V^T by transposing reads),
-// staged by the two halves of the workgroup.  fp32 (NWV = 4): threads 0..127 move K (padded
-// rows), 128..255 move V (transposed).
+// bf16 (NWV = 8 at head size 128, one workgroup per CU; 4 below, two per CU: two waves per
+// SIMD either way): K and V as swizzled row tiles (V^T by transposing reads), staged by the two
+// halves of the workgroup.  fp32 (NWV = 4): threads 0..127 move K (padded rows), 128..255 move
+// V (transposed).
 // BOUNDED: every score is at most `bound` (q and k RMS-normalized per head, so |q.k|/sqrt(Hd) <=
 // sqrt(Hd)): the softmax weights are taken against that fixed reference, 2^(sl2 (s - bound)) in
 // [2^(-2 sl2 bound), 1], and no running maximum is kept.
@@ -1087,10 +1088,12 @@ gpt_status launch_attn_fwd(const T* qkv, T* out, float* lse2, int B, int Tn, int
   // after rounding each element to bf16, so every scaled score is below sqrt(hd) (1 + 2^-7).
   const float bound = sqrtf((float)hd) * (1.f + 1.f / 128.f);
   // 32 queries per wave, two waves per SIMD so that one wave's softmax overlaps the other's
-  // MFMAs: bf16 runs 8-wave workgroups (one per CU), fp32 4-wave workgroups (two per CU).
+  // MFMAs: bf16 at head size 128 runs 8-wave workgroups (one per CU; as two 4-wave workgroups
+  // the staging registers spill and the d32 shape ran 172 -> 304 us), smaller heads and fp32
+  // 4-wave workgroups (two per CU; GPT-2-small 27.7 -> 26.1 us against 8 waves).
   gpt_status st = dispatch_hd<T>(hd, [&](auto HD) {
     constexpr int hdv = decltype(HD)::value;
-    constexpr int NWV = sizeof(T) == 2 ? 8 : 4;
+    constexpr int NWV = (sizeof(T) == 2 && hdv > 64) ? 8 : 4;
     const dim3 grid(H * B, cdiv(Tn, 32 * NWV));
     if (qk_normed)
       attn_fwd_kernel<T, hdv, NWV, true><<<grid, 64 * NWV, 0, s>>>(qkv, out, lse2, Tn, H, sl2, bound);
