@@ -525,9 +525,12 @@ struct Stage {
 
 // Logical tile order: blocks are dispatched round-robin over the 8 XCDs, so block b runs on
 // XCD b % 8.  Give XCD x the contiguous range of logical tiles x*per .. x*per+per-1, and walk
-// tiles in groups of GROUP_M row-tiles so that consecutive tiles share A and B panels.
+// tiles in groups of GROUP_M row-tiles so that consecutive tiles share A and B panels.  Groups
+// of 4 measured best on the d32 products (against 8: dReLU^2 dgrad 549 -> 522-529 us, out
+// dgrad 128 -> 121-124 us, down projection 546-555 -> 534-541 us; 2 about the same as 4, 1 and
+// 16 slower) and neutral on GPT-2-small's.
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int GROUP_M = 8;
+  constexpr int GROUP_M = 4;
   const int nb = gridDim.x, b = blockIdx.x;
   const int L = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
   const int per_group = GROUP_M * tiles_n;
