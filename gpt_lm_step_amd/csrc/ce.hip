@@ -336,7 +336,7 @@ gpt_status launch_ce(T* z, long long ldz, const int32_t* tgt, long long rows, in
   else if (g <= 2048) CE_CASE(256, 8);
   else if (g <= 4096) CE_CASE(512, 8);
   else if (g <= 6656) CE_CASE(512, 13);  // V <= 53,248 (GPT-2's 50,304: 94% of the slots used)
-  else if (g <= 8192) CE_CASE(512, 16);
+  else if (g <= 8192) CE_CASE(1024, 8);  // 16 waves: 827 -> 793 us at 16384 x 65536 (512 x 16)
   else return fail(GPT_ESHAPE, "vocab above 65536 is not supported");
 #undef CE_CASE
 #undef CE_LAUNCH
