@@ -49,7 +49,7 @@ class gpt_config(C.Structure):
                                          "d_mlp", "vocab", "seq_len", "batch", "dtype")] + \
                [("rms_eps", C.c_float), ("rope_base", C.c_float), ("softcap", C.c_float)] + \
                [(n, C.c_int32) for n in ("qk_norm", "has_x0_add", "has_v_add", "has_trigram",
-                                         "ce_chunk_tokens")]
+                                         "ce_chunk_tokens", "wgrad_stream")]
 
 
 class gpt_profile_entry(C.Structure):
@@ -153,7 +153,7 @@ def make_config(cfg: GPTConfig) -> gpt_config:
     return gpt_config(cfg.n_layer, cfg.d_model, cfg.n_head, cfg.n_kv_head, cfg.head_dim,
                       cfg.d_mlp, cfg.vocab, cfg.seq_len, cfg.batch, cfg.dtype, cfg.rms_eps,
                       cfg.rope_base, cfg.softcap, cfg.qk_norm, cfg.has_x0_add, cfg.has_v_add,
-                      cfg.has_trigram, cfg.ce_chunk_tokens)
+                      cfg.has_trigram, cfg.ce_chunk_tokens, cfg.wgrad_stream)
 
 
 def gpt_param_layout(cfg: GPTConfig) -> Tuple[List[Tuple[str, int, Tuple[int, int]]], int]:

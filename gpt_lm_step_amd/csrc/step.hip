@@ -56,6 +56,7 @@ gpt_status validate(const gpt_config* c) {
   if (c->dtype != GPT_F32 && c->dtype != GPT_BF16) return fail(GPT_EINVAL, "bad dtype");
   if (c->ce_chunk_tokens < 0 || c->ce_chunk_tokens % 64)
     return fail(GPT_ESHAPE, "ce_chunk_tokens must be 0 or a positive multiple of 64");
+  if (c->wgrad_stream < -1 || c->wgrad_stream > 1) return fail(GPT_EINVAL, "wgrad_stream must be -1, 0 or 1");
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f) || !(c->softcap >= 0.f))
     return fail(GPT_ERANGE, "rms_eps, rope_base or softcap out of range");
   return GPT_OK;
@@ -67,6 +68,14 @@ namespace {
 // Tokens of one head/cross-entropy chunk: the caller's choice, capped so that the bf16/fp32
 // logits chunk spans at most 2 GiB (the most one GEMM operand may span); by default all tokens
 // when they fit.
+// Whether the blocks' weight gradients get a stream of their own: on the bf16 path unless the
+// caller says no (measured on MI355X: GPT-2-small step 11.46 -> 10.61 ms, whose 128 x 128 tiles
+// and short products leave room beside each other; d32 186.9 -> 186.3 ms, where the 256 x 256
+// tiles fill the CUs and only the edges of the launches overlap).
+bool use_wgrad_stream(const gpt_config& c) {
+  return c.dtype == GPT_BF16 && c.wgrad_stream >= 0;
+}
+
 long long ce_chunk_rows(const gpt_config& c) {
   const long long N = (long long)c.batch * c.seq_len;
   const long long esz = c.dtype == GPT_BF16 ? 2 : 4;
@@ -176,6 +185,17 @@ struct gpt_ctx {
   void* ws;
   size_t ws_bytes;
   gpt::Prof prof;
+  // Weight gradients of the blocks on a stream of their own (when `side` is set), so that they
+  // run beside the input-gradient chain; fork: the side stream waits for the caller's stream so
+  // far; ev_dw / ev_ow: the caller's stream waits for the down / out weight gradient of a layer
+  // before overwriting the gradient rows they read; ev_end: the join after the last layer.
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, ev_dw = nullptr, ev_ow = nullptr, ev_end = nullptr;
+  ~gpt_ctx() {
+    for (hipEvent_t e : {fork, ev_dw, ev_ow, ev_end})
+      if (e) (void)hipEventDestroy(e);
+    if (side) (void)hipStreamDestroy(side);
+  }
 };
 
 namespace gpt {
@@ -200,16 +220,40 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
   const double pairs = (double)Bn * H * Tn * (Tn + 1) / 2.0;  // causal (query, key) pairs
   const T* cos_t = (const T*)p.cos_t;
   const T* sin_t = (const T*)p.sin_t;
-  // Run one stage; with profiling on, bracket it by events and record its algorithmic work.
-  auto run = [&](const char* name, double flops, double bytes, auto&& fn) -> gpt_status {
+  // Run one stage on stream `on`; with profiling on, bracket it by events and record its
+  // algorithmic work.
+  auto run_on = [&](hipStream_t on, const char* name, double flops, double bytes,
+                    auto&& fn) -> gpt_status {
     if (!prof.on) return fn();
     hipEvent_t e0 = prof.get(), e1 = prof.get();
     if (!e0 || !e1) return fail(GPT_EHIP, "profiling: hipEventCreate failed");
-    (void)hipEventRecord(e0, s);
+    (void)hipEventRecord(e0, on);
     gpt_status st = fn();
-    (void)hipEventRecord(e1, s);
+    (void)hipEventRecord(e1, on);
     prof.recs.push_back({name, flops, bytes, e0, e1});
     return st;
+  };
+  auto run = [&](const char* name, double flops, double bytes, auto&& fn) -> gpt_status {
+    return run_on(s, name, flops, bytes, fn);
+  };
+  // The blocks' weight gradients go to ws (the side stream, or s itself): fork() makes ws wait
+  // for everything issued to s so far; mark(e) records e after what ws holds so far, and
+  // await_mark(e) makes s wait for it.
+  const bool side = ctx->side != nullptr;
+  hipStream_t ws = side ? ctx->side : s;
+  auto fork = [&]() -> gpt_status {
+    if (!side) return GPT_OK;
+    if (hipEventRecord(ctx->fork, s) != hipSuccess || hipStreamWaitEvent(ws, ctx->fork, 0) != hipSuccess)
+      return fail(GPT_EHIP, "weight-gradient stream: fork failed");
+    return GPT_OK;
+  };
+  auto mark = [&](hipEvent_t e) -> gpt_status {
+    if (side && hipEventRecord(e, ws) != hipSuccess) return fail(GPT_EHIP, "weight-gradient stream: record failed");
+    return GPT_OK;
+  };
+  auto await_mark = [&](hipEvent_t e) -> gpt_status {
+    if (side && hipStreamWaitEvent(s, e, 0) != hipSuccess) return fail(GPT_EHIP, "weight-gradient stream: wait failed");
+    return GPT_OK;
   };
   auto mm = [](double m, double n, double k) { return 2.0 * m * n * k; };
 #define TRY(x)                          \
@@ -218,6 +262,8 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
     if (st_ != GPT_OK) return st_;      \
   } while (0)
 #define STAGE(name, flops, bytes, ...) TRY(run(name, flops, bytes, [&]() { return __VA_ARGS__; }))
+#define SIDE_STAGE(name, flops, bytes, ...) \
+  TRY(run_on(ws, name, flops, bytes, [&]() { return __VA_ARGS__; }))
 
   // value addend u = v_add + tri_rows wtri^T (fp32), shared by every layer
   const float* u = nullptr;
@@ -321,31 +367,41 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
     LayerBufs& b = p.L[l];
     const T *a = (const T*)b.a, *qkv = (const T*)b.qkv, *o = (const T*)b.o, *bb = (const T*)b.b,
             *act = (const T*)b.act;
-    // MLP: x_out = x_mid + relu(b Wfc^T)^2 Wpr^T
+    // MLP: x_out = x_mid + relu(b Wfc^T)^2 Wpr^T.  With the side stream, the weight gradients
+    // of a layer run beside its input-gradient chain; s waits for the down (out) weight gradient
+    // before the norm backward overwrites the dx_t rows it reads.  The other buffers a weight
+    // gradient reads (dact, dqkv) are next written one layer later, after s has already waited
+    // for a later item of the in-order side stream.
+    TRY(fork());
+    SIDE_STAGE("down_wgrad", mm(D, F, N), 0,
+               gemm_wgrad<G_DOWN_WGRAD, T>(false, false, D, F, (int)N, dx_t, D, act, F,
+                                           EpiStoreF32{G + Ly.wpr[l], F, beta}, p.splitk,
+                                           p.splitk_floats, ws));
+    TRY(mark(ctx->ev_dw));
     STAGE("down_dgrad", mm(N, F, D), 0,
           gemm<G_DOWN_DGRAD, T>(true, false, (int)N, F, D, dx_t, D, P + Ly.wpr[l], F,
                                 EpiDRelu2<T>{act, dact, F}, s));
-    STAGE("down_wgrad", mm(D, F, N), 0,
-          gemm_wgrad<G_DOWN_WGRAD, T>(false, false, D, F, (int)N, dx_t, D, act, F,
-                                      EpiStoreF32{G + Ly.wpr[l], F, beta}, p.splitk,
-                                      p.splitk_floats, s));
+    TRY(fork());
+    SIDE_STAGE("up_wgrad", mm(F, D, N), 0,
+               gemm_wgrad<G_UP_WGRAD, T>(false, false, F, D, (int)N, dact, F, bb, D,
+                                         EpiStoreF32{G + Ly.wfc[l], D, beta}, p.splitk,
+                                         p.splitk_floats, ws));
     STAGE("up_dgrad", mm(N, D, F), 0,
           gemm<G_UP_DGRAD, T>(true, false, (int)N, D, F, dact, F, P + Ly.wfc[l], D,
                               EpiStoreF32{p.db, D, 0}, s));
-    STAGE("up_wgrad", mm(F, D, N), 0,
-          gemm_wgrad<G_UP_WGRAD, T>(false, false, F, D, (int)N, dact, F, bb, D,
-                                    EpiStoreF32{G + Ly.wfc[l], D, beta}, p.splitk,
-                                    p.splitk_floats, s));
+    TRY(await_mark(ctx->ev_dw));
     STAGE("rmsnorm_bwd", 0, ND * (16 + es) + 4.0 * N,
           launch_rms_bwd<T>(b.x_mid, b.rstd_b, p.db, p.dx, p.dx, dx_t, N, D, s));
     // attention: x_mid = x_in + O Wo^T
+    TRY(fork());
+    SIDE_STAGE("out_wgrad", mm(D, D, N), 0,
+               gemm_wgrad<G_OUT_WGRAD, T>(false, false, D, D, (int)N, dx_t, D, o, D,
+                                          EpiStoreF32{G + Ly.wo[l], D, beta}, p.splitk,
+                                          p.splitk_floats, ws));
+    TRY(mark(ctx->ev_ow));
     STAGE("out_dgrad", mm(N, D, D), 0,
           gemm<G_OUT_DGRAD, T>(true, false, (int)N, D, D, dx_t, D, P + Ly.wo[l], D,
                                EpiStore<T>{dO, D}, s));
-    STAGE("out_wgrad", mm(D, D, N), 0,
-          gemm_wgrad<G_OUT_WGRAD, T>(false, false, D, D, (int)N, dx_t, D, o, D,
-                                     EpiStoreF32{G + Ly.wo[l], D, beta}, p.splitk,
-                                     p.splitk_floats, s));
     STAGE("attn_bwd_dq", 2.0 * pairs * hd, 0,
           launch_attn_bwd_stage<T>(0, qkv, o, dO, b.lse, p.dqsum, dqkv, Bn, Tn, H, hd, s));
     STAGE("attn_bwd_dkdv", 8.0 * pairs * hd, 0,
@@ -355,16 +411,21 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
     if (vadd)
       STAGE("dvadd_accum", 0, ND * (es + (l != Lc - 1 ? 8 : 4)),
             launch_accum_rows<T>(p.dU, dqkv + 2 * D, 3LL * D, N, D, l != Lc - 1, s));
+    TRY(fork());
+    SIDE_STAGE("qkv_wgrad", mm(3 * D, D, N), 0,
+               gemm_wgrad<G_QKV_WGRAD, T>(false, false, 3 * D, D, (int)N, dqkv, 3 * D, a, D,
+                                          EpiStoreF32{G + Ly.wqkv[l], D, beta}, p.splitk,
+                                          p.splitk_floats, ws));
     STAGE("qkv_dgrad", mm(N, D, 3 * D), 0,
           gemm<G_QKV_DGRAD, T>(true, false, (int)N, D, 3 * D, dqkv, 3 * D, P + Ly.wqkv[l], D,
                                EpiStoreF32{p.db, D, 0}, s));
-    STAGE("qkv_wgrad", mm(3 * D, D, N), 0,
-          gemm_wgrad<G_QKV_WGRAD, T>(false, false, 3 * D, D, (int)N, dqkv, 3 * D, a, D,
-                                     EpiStoreF32{G + Ly.wqkv[l], D, beta}, p.splitk,
-                                     p.splitk_floats, s));
+    TRY(await_mark(ctx->ev_ow));
     STAGE("rmsnorm_bwd", 0, ND * (16 + es) + 4.0 * N,
           launch_rms_bwd<T>(b.x_in, b.rstd_a, p.db, p.dx, p.dx, dx_t, N, D, s));
   }
+  // every weight gradient of the blocks is written (and the split-K workspace free) from here on
+  TRY(mark(ctx->ev_end));
+  TRY(await_mark(ctx->ev_end));
 
   // ---------------- embedding, x0 addend, value addend
   if (c.has_x0_add && d_x0_add)
@@ -387,6 +448,7 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
                                        p.splitk_floats, s));
     }
   }
+#undef SIDE_STAGE
 #undef STAGE
 #undef TRY
   return GPT_OK;
@@ -446,6 +508,15 @@ gpt_status gpt_init(const gpt_config* cfg, void* workspace, size_t ws_bytes, hip
   Plan plan = carve_plan(*cfg, cv);
   if (!cv.ok) return fail(GPT_EWORKSPACE, "gpt_init: workspace smaller than gpt_workspace_bytes");
   gpt_ctx* ctx = new gpt_ctx{*cfg, make_layout(*cfg), plan, workspace, ws_bytes};
+  if (use_wgrad_stream(*cfg)) {
+    bool ok = hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking) == hipSuccess;
+    for (hipEvent_t* e : {&ctx->fork, &ctx->ev_dw, &ctx->ev_ow, &ctx->ev_end})
+      ok = ok && hipEventCreateWithFlags(e, hipEventDisableTiming) == hipSuccess;
+    if (!ok) {
+      delete ctx;
+      return fail(GPT_EHIP, "gpt_init: weight-gradient stream or events could not be created");
+    }
+  }
   if (cfg->dtype == GPT_BF16)
     st = launch_rope_table<bf16>((bf16*)plan.cos_t, (bf16*)plan.sin_t, cfg->seq_len, cfg->head_dim,
                                  cfg->rope_base, stream);

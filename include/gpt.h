@@ -70,6 +70,13 @@ typedef struct {
                               (the logits chunk is [chunk, vocab] in dtype); the result does not
                               depend on the chunking beyond fp32 summation order of the head's
                               weight gradient. */
+  int32_t wgrad_stream;    /* where the blocks' weight-gradient products run in the backward
+                              (bf16 only; fp32 always uses the caller's stream): 1 = a stream of
+                              their own, created by gpt_init, beside the input-gradient chain
+                              (the caller's stream waits for it before gpt_fwd_bwd's work
+                              returns to it); 0 (the default) is the same; -1 = the caller's
+                              stream only.  Results are bitwise the same either way: only the
+                              overlap of independent kernels changes. */
 } gpt_config;
 
 /* One entry of the flat parameter layout. */
@@ -97,7 +104,9 @@ gpt_status gpt_workspace_bytes(const gpt_config* cfg, size_t* bytes);
 /* Create a step context over a caller-provided workspace (256-byte aligned, at least
  * gpt_workspace_bytes).  Enqueues one kernel on `stream` that fills the rotary tables
  * (cos/sin of t * base^(-2i/head_dim), stored in `dtype`, as _precompute_rotary_embeddings
- * on the nanochat page).  *out [host] receives the context.  Not thread-safe per context. */
+ * on the nanochat page).  On the bf16 path (unless cfg->wgrad_stream is -1) it also creates the
+ * context's weight-gradient stream (default priority) and four events, released by
+ * gpt_destroy.  *out [host] receives the context.  Not thread-safe per context. */
 gpt_status gpt_init(const gpt_config* cfg, void* workspace, size_t ws_bytes, hipStream_t stream,
                     gpt_ctx** out);
 
@@ -115,7 +124,9 @@ gpt_status gpt_init(const gpt_config* cfg, void* workspace, size_t ws_bytes, hip
  *            grad_scale * loss w.r.t. x0_add and v_add (u), always overwritten.  These feed
  *            bigram_bwd_update; no [rows, D] table gradient exists anywhere.
  *   loss     fp32 device scalar: mean cross-entropy over valid targets (not scaled).
- * Stream-ordered; never synchronises. */
+ * Stream-ordered; never synchronises.  With the context's weight-gradient stream, that stream
+ * first waits for `stream` and `stream` waits for it before the call's last launches, so
+ * everything the call writes is ordered on `stream` as usual. */
 gpt_status gpt_fwd_bwd(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
                        const void* params, float* grads, float grad_scale, int32_t accumulate,
                        const void* x0_add, const void* v_add, const void* tri_rows,

@@ -57,6 +57,7 @@ def test_workspace_sizes_are_plausible():
     ("seq_len", 100, B.GPT_ESHAPE), ("dtype", 7, B.GPT_EINVAL), ("n_layer", 0, B.GPT_ESHAPE),
     ("vocab", 65536 + 64, B.GPT_ESHAPE), ("d_model", 4096, B.GPT_ESHAPE),
     ("ce_chunk_tokens", 100, B.GPT_ESHAPE), ("ce_chunk_tokens", -64, B.GPT_ESHAPE),
+    ("wgrad_stream", 2, B.GPT_EINVAL), ("wgrad_stream", -2, B.GPT_EINVAL),
 ])
 def test_invalid_configs_are_rejected(field, value, status):
     c = B.make_config(configs.TINY)

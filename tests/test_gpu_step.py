@@ -190,6 +190,39 @@ def test_gpt2_small_bf16_full_launch_sampled_sequences():
     assert B.gpt_check_errors(step.ctx) == 0        # no kernel wrote past its buffer
 
 
+@pytest.mark.parametrize("base", ["speedrun-bf16", "d32-small-batch"])
+def test_weight_gradient_stream_changes_no_bit(base):
+    """The blocks' weight-gradient products on a stream of their own give bitwise the results of
+    the same step on the caller's stream alone: two micro-batches (overwrite, then accumulate
+    with grad_scale 1/2), loss, every gradient and the addend gradients compared bit for bit.
+    Shapes: the speedrun micro-batch (GPT-2-small with both table addends and the trigram
+    projection, full 8 x 1024 launch) and the d32 layer shapes with 4 layers and 2 x 2048
+    tokens."""
+    if base == "speedrun-bf16":
+        cfg = configs.SPEEDRUN
+    else:
+        cfg = configs.D32.replace(n_layer=4, batch=2)
+    params = inputs.model_params(cfg, 106)
+    N, D = cfg.tokens, cfg.d_model
+    vadd = cfg.has_v_add or cfg.has_trigram
+    adds = [inputs.addend(21 + i, N, D, s, True) if on else None
+            for i, (on, s) in enumerate(((cfg.has_x0_add, 0.02), (cfg.has_v_add, 0.02),
+                                         (cfg.has_trigram, 1.0)))]
+    steps = [Step(cfg.replace(wgrad_stream=w), params) for w in (1, -1)]
+    for mb in range(2):
+        tok = inputs.step_tokens(cfg, 30 + mb)
+        for st in steps:
+            st.loss_v = st.run(tok, tok[:, 1:], *adds, grad_scale=0.5, accumulate=mb)
+        a, b = steps
+        assert a.loss_v == b.loss_v, mb
+        assert torch.equal(a.grads, b.grads), mb
+        if cfg.has_x0_add:
+            assert torch.equal(a.d_x0, b.d_x0), mb
+        if vadd:
+            assert torch.equal(a.d_v, b.d_v), mb
+    assert torch.isfinite(steps[0].grads).all()
+
+
 @pytest.mark.timeout(900)
 def test_d32_bf16_full_launch_one_full_sequence():
     """The d32 step at the size the bench times (B=8, T=2048, V=65536, 32 layers, device-drawn
