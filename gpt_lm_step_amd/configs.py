@@ -41,7 +41,7 @@ class GPTConfig:
     has_v_add: int = 0
     has_trigram: int = 0
     ce_chunk_tokens: int = 0     # LM-head / cross-entropy chunk (0: library default)
-    wgrad_stream: int = 0        # weight gradients on their own stream: 0 or 1 yes (bf16), -1 no
+    wgrad_stream: int = 0        # weight gradients on their own stream: 1 yes, -1 no, 0 library
     name: str = ""
 
     @property

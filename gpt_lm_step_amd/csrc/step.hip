@@ -68,12 +68,16 @@ namespace {
 // Tokens of one head/cross-entropy chunk: the caller's choice, capped so that the bf16/fp32
 // logits chunk spans at most 2 GiB (the most one GEMM operand may span); by default all tokens
 // when they fit.
-// Whether the blocks' weight gradients get a stream of their own: on the bf16 path unless the
-// caller says no (measured on MI355X: GPT-2-small step 11.46 -> 10.61 ms, whose 128 x 128 tiles
-// and short products leave room beside each other; d32 186.9 -> 186.3 ms, where the 256 x 256
-// tiles fill the CUs and only the edges of the launches overlap).
+// Whether the blocks' weight gradients get a stream of their own (bf16 path only): the caller's
+// choice, else where the MLP-up weight gradient's plan uses 128 x 128 tiles (two workgroups per
+// CU, so the products of both streams share the CUs).  Measured on MI355X: GPT-2-small step
+// 11.46 -> 10.61 ms; d32 (256 x 256 tiles, which fill the CUs, so only the ends of the launches
+// overlap) 186.9 -> 186.3 ms, not worth stretching its kernels' individual durations.
 bool use_wgrad_stream(const gpt_config& c) {
-  return c.dtype == GPT_BF16 && c.wgrad_stream >= 0;
+  if (c.dtype != GPT_BF16 || c.wgrad_stream < 0) return false;
+  if (c.wgrad_stream > 0) return true;
+  const long long n = (long long)c.batch * c.seq_len;
+  return !gemm_detail::split_plan(c.d_mlp, c.d_model, (int)n).big;
 }
 
 long long ce_chunk_rows(const gpt_config& c) {
@@ -239,7 +243,8 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
   // The blocks' weight gradients go to ws (the side stream, or s itself): fork() makes ws wait
   // for everything issued to s so far; mark(e) records e after what ws holds so far, and
   // await_mark(e) makes s wait for it.
-  const bool side = ctx->side != nullptr;
+  // (a profiled step stays on one stream, so that each stage's events time its own kernels)
+  const bool side = ctx->side != nullptr && !prof.on;
   hipStream_t ws = side ? ctx->side : s;
   auto fork = [&]() -> gpt_status {
     if (!side) return GPT_OK;

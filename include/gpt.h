@@ -74,9 +74,11 @@ typedef struct {
                               (bf16 only; fp32 always uses the caller's stream): 1 = a stream of
                               their own, created by gpt_init, beside the input-gradient chain
                               (the caller's stream waits for it before gpt_fwd_bwd's work
-                              returns to it); 0 (the default) is the same; -1 = the caller's
-                              stream only.  Results are bitwise the same either way: only the
-                              overlap of independent kernels changes. */
+                              returns to it); -1 = the caller's stream only; 0 = the library's
+                              choice (its own stream where those products use 128 x 128 tiles,
+                              as in the GPT-2-small shapes).  Profiled steps (gpt_profile) stay
+                              on the caller's stream.  Results are bitwise the same either way:
+                              only the overlap of independent kernels changes. */
 } gpt_config;
 
 /* One entry of the flat parameter layout. */
@@ -104,9 +106,9 @@ gpt_status gpt_workspace_bytes(const gpt_config* cfg, size_t* bytes);
 /* Create a step context over a caller-provided workspace (256-byte aligned, at least
  * gpt_workspace_bytes).  Enqueues one kernel on `stream` that fills the rotary tables
  * (cos/sin of t * base^(-2i/head_dim), stored in `dtype`, as _precompute_rotary_embeddings
- * on the nanochat page).  On the bf16 path (unless cfg->wgrad_stream is -1) it also creates the
- * context's weight-gradient stream (default priority) and four events, released by
- * gpt_destroy.  *out [host] receives the context.  Not thread-safe per context. */
+ * on the nanochat page).  When the weight gradients get a stream of their own (see
+ * gpt_config.wgrad_stream) it also creates that stream (default priority) and four events,
+ * released by gpt_destroy.  *out [host] receives the context.  Not thread-safe per context. */
 gpt_status gpt_init(const gpt_config* cfg, void* workspace, size_t ws_bytes, hipStream_t stream,
                     gpt_ctx** out);
 
