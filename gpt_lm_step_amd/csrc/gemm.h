@@ -403,7 +403,7 @@ enum GemmSite {
   G_TEST = 0, G_QKV, G_OUT, G_UP, G_DOWN, G_HEAD, G_HEAD_DGRAD, G_HEAD_WGRAD, G_DOWN_DGRAD,
   G_DOWN_WGRAD, G_UP_DGRAD, G_UP_WGRAD, G_OUT_DGRAD, G_OUT_WGRAD, G_QKV_DGRAD, G_QKV_WGRAD,
   G_TRI, G_TRI_WGRAD, G_NS_GRAM, G_NS_POLY, G_NS_APPLY, G_INF_QKV, G_INF_OUT, G_INF_UP,
-  G_INF_DOWN, G_INF_HEAD
+  G_INF_DOWN, G_INF_HEAD, G_QKV_OUT_WGRAD
 };
 
 // Passes of an epilogue row slice whose loads may be in flight together (Epi::pass_group when
@@ -529,9 +529,11 @@ struct Stage {
 // of 4 measured best on the d32 products (against 8: dReLU^2 dgrad 549 -> 522-529 us, out
 // dgrad 128 -> 121-124 us, down projection 546-555 -> 534-541 us; 2 about the same as 4, 1 and
 // 16 slower) and neutral on GPT-2-small's.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+// Block b of nb blocks (a paired launch numbers each problem's blocks from 0; its first
+// problem's block count is a multiple of 8, so block b still runs on XCD b % 8).
+__device__ __forceinline__ void tile_coords(int nb, int b, int tiles_m, int tiles_n, int& tm,
+                                            int& tn) {
   constexpr int GROUP_M = 4;
-  const int nb = gridDim.x, b = blockIdx.x;
   const int L = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
   const int per_group = GROUP_M * tiles_n;
   const int grp = L / per_group;
@@ -568,7 +570,7 @@ __global__ __launch_bounds__(THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_
   __shared__ __attribute__((aligned(16))) T lds[2][(BM + BN) * C::PITCH];
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  tile_coords(gridDim.x, blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE;
   const int wm = (w / 2) * (BM / 2), wn = (w % 2) * (BN / 2);
@@ -775,12 +777,13 @@ __device__ __forceinline__ void wait_vm_lds() {
 // behind the MFMAs.  One barrier per K tile (after this wave's DMA of tile kt has landed, so all
 // waves' have; the stage read in the previous iteration is then free for the next DMA).  The
 // 256 x 256 tile runs 8 waves, two per SIMD; the 128 x 128 tile 4 waves, two workgroups per CU.
-template <int BM, int BN, int WGM, int WGN, int BK, int NS, bool A_KC, bool B_KC, class Epi,
-          int SITE>
-__global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_dma_kernel(
+// The workgroup computes tile `vb` of the `nvb` tiles of its problem (blockIdx.x and gridDim.x
+// for a plain launch).
+template <int BM, int BN, int WGM, int WGN, int BK, int NS, bool A_KC, bool B_KC, class Epi>
+__device__ __forceinline__ void gemm_dma_tile(
     const bf16* A, long long lda, const bf16* B, long long ldb, int M,
     int N, int K, uint32_t a_bytes, uint32_t b_bytes, Epi epi, int kps, long long a_bs,
-    long long b_bs) {
+    long long b_bs, int vb, int nvb) {
   constexpr int NW = WGM * WGN, WTM = BM / WGM, WTN = BN / WGN;
   // batch z = blockIdx.z: operands at A + z * a_bs, B + z * b_bs; epilogues that hold batched
   // outputs move their pointers themselves
@@ -802,7 +805,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
   if constexpr (is_symmetric<Epi>::value) tri_coords(tiles_m, tm, tn);
-  else tile_coords(tiles_m, tiles_n, tm, tn);
+  else tile_coords(nvb, vb, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE;
   const int wm = (w / WGN) * WTM, wn = (w % WGN) * WTN;
@@ -1028,6 +1031,41 @@ __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) voi
   else epilogue(halves[NS + (w - NS * WPA) / WPB] + ((w - NS * WPA) % WPB) * (REGION / 4));
 }
 
+template <int BM, int BN, int WGM, int WGN, int BK, int NS, bool A_KC, bool B_KC, class Epi,
+          int SITE>
+__global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_dma_kernel(
+    const bf16* A, long long lda, const bf16* B, long long ldb, int M,
+    int N, int K, uint32_t a_bytes, uint32_t b_bytes, Epi epi, int kps, long long a_bs,
+    long long b_bs) {
+  gemm_dma_tile<BM, BN, WGM, WGN, BK, NS, A_KC, B_KC, Epi>(A, lda, B, ldb, M, N, K, a_bytes,
+                                                           b_bytes, epi, kps, a_bs, b_bs,
+                                                           blockIdx.x, gridDim.x);
+}
+
+// One operand pair of a paired launch (the same layouts, tile size and epilogue type).
+template <class Epi>
+struct GemmProb {
+  const bf16 *A, *B;
+  long long lda, ldb;
+  int M, N, K;
+  uint32_t a_bytes, b_bytes;
+  Epi epi;
+  int tiles;
+};
+// Two independent products in one launch: blocks 0 .. p0.tiles-1 compute p0's tiles, the rest
+// p1's (each walked in its own XCD-grouped order), so that two products that would each leave
+// CUs idle fill one round of the chip together.
+template <int BM, int BN, int WGM, int WGN, int BK, int NS, bool A_KC, bool B_KC, class Epi,
+          int SITE>
+__global__ __launch_bounds__(64 * WGM * WGN, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_dma_pair_kernel(
+    GemmProb<Epi> p0, GemmProb<Epi> p1) {
+  const bool second = (int)blockIdx.x >= p0.tiles;
+  const GemmProb<Epi>& p = second ? p1 : p0;
+  gemm_dma_tile<BM, BN, WGM, WGN, BK, NS, A_KC, B_KC, Epi>(
+      p.A, p.lda, p.B, p.ldb, p.M, p.N, p.K, p.a_bytes, p.b_bytes, p.epi, p.K, 0, 0,
+      (int)blockIdx.x - (second ? p0.tiles : 0), p.tiles);
+}
+
 // Calls f with an epilogue whose loads do not depend on run-time flags: accumulate vs overwrite
 // and present vs absent addends become distinct types (a load that a flag may skip leaves the
 // kernel unable to count its outstanding loads, so it waits for all of them).
@@ -1052,6 +1090,19 @@ inline void with_static_epi(const EpiAddRows<T>& e, F&& f) {
 // Bytes spanned by an operand of `rows` x K (KC: rows of ld; RC: K rows of ld).
 inline long long operand_bytes(bool kc, long long rows, long long K, long long ld, long long es) {
   return (kc ? (rows - 1) * ld + K : (K - 1) * ld + rows) * es;
+}
+
+// Compute units of the current device (cached per device; 256 if the query fails).
+inline unsigned resident_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = cus;
+  }
+  return (unsigned)cached[dev];
 }
 
 template <int BM, int BN, int WGM, int WGN, class Epi, int SITE>
@@ -1300,6 +1351,51 @@ inline gpt_status gemm_wgrad(bool a_kc, bool b_kc, int M, int N, int K, const T*
                                                                             epi.ldo, M, N, epi.beta);
     return check_launch("gemm split-K");
   }
+}
+
+// Two fp32-output bf16 products with row-contiguous operands (weight gradients dW = dY^T X over
+// the tokens) in one launch of 256 x 256 tiles, unsplit: for pairs whose tiles together fill
+// about one round of the CUs while each alone would leave CUs idle or need split-K partials
+// (the d32 q/k/v and out weight gradients: 192 + 64 tiles).  Same argument rules as gemm();
+// both outputs overwrite or both accumulate (beta).
+template <int SITE>
+inline gpt_status gemm_wgrad_pair(int M0, int N0, int K0, const bf16* A0, long long lda0,
+                                  const bf16* B0, long long ldb0, const EpiStoreF32& e0, int M1,
+                                  int N1, int K1, const bf16* A1, long long lda1, const bf16* B1,
+                                  long long ldb1, const EpiStoreF32& e1, hipStream_t s) {
+  if (e0.beta != e1.beta) return fail(GPT_EINVAL, "gemm_wgrad_pair: both outputs take the same beta");
+  const int Ms[2] = {M0, M1}, Ns[2] = {N0, N1}, Ks[2] = {K0, K1};
+  const bf16* As[2] = {A0, A1};
+  const bf16* Bs[2] = {B0, B1};
+  const long long ldas[2] = {lda0, lda1}, ldbs[2] = {ldb0, ldb1};
+  const EpiStoreF32* es[2] = {&e0, &e1};
+  int tiles[2];
+  for (int i = 0; i < 2; ++i) {
+    if (Ms[i] <= 0 || Ns[i] <= 0 || Ks[i] <= 0 || Ks[i] % 8 || Ms[i] % 8 || Ns[i] % 8)
+      return fail(GPT_ESHAPE, "gemm_wgrad_pair: M, N, K must be positive multiples of 8");
+    if (ldas[i] % 8 || ldbs[i] % 8 || es[i]->ldo % 4)
+      return fail(GPT_ESHAPE, "gemm_wgrad_pair: bad leading dimensions");
+    if (((uintptr_t)As[i] | (uintptr_t)Bs[i] | (uintptr_t)es[i]->out) % 16)
+      return fail(GPT_EINVAL, "gemm_wgrad_pair: operands must be 16-byte aligned");
+    if (gemm_detail::operand_bytes(false, Ms[i], Ks[i], ldas[i], 2) > (1LL << 31) ||
+        gemm_detail::operand_bytes(false, Ns[i], Ks[i], ldbs[i], 2) > (1LL << 31))
+      return fail(GPT_ESHAPE, "gemm: each operand must span at most 2 GiB");
+    tiles[i] = (int)(cdiv(Ms[i], 256) * cdiv(Ns[i], 256));
+  }
+  if (tiles[0] % 8) return fail(GPT_ESHAPE, "gemm_wgrad_pair: the first product needs a multiple of 8 tiles");
+  auto go = [&](auto proto) -> gpt_status {
+    using E = decltype(proto);
+    gemm_detail::GemmProb<E> p[2];
+    for (int i = 0; i < 2; ++i)
+      p[i] = gemm_detail::GemmProb<E>{As[i], Bs[i], ldas[i], ldbs[i], Ms[i], Ns[i], Ks[i],
+                         (uint32_t)gemm_detail::operand_bytes(false, Ms[i], Ks[i], ldas[i], 2),
+                         (uint32_t)gemm_detail::operand_bytes(false, Ns[i], Ks[i], ldbs[i], 2),
+                         E{es[i]->out, es[i]->ldo}, tiles[i]};
+    gemm_detail::gemm_dma_pair_kernel<256, 256, 2, 4, 32, 4, false, false, E, SITE>
+        <<<dim3((unsigned)(tiles[0] + tiles[1])), 64 * 2 * 4, 0, s>>>(p[0], p[1]);
+    return check_launch("gemm_wgrad_pair");
+  };
+  return e0.beta ? go(EpiAccF32{}) : go(EpiPutF32{});
 }
 
 }  // namespace gpt

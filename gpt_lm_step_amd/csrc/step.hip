@@ -246,6 +246,15 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
   // (a profiled step stays on one stream, so that each stage's events time its own kernels)
   const bool side = ctx->side != nullptr && !prof.on;
   hipStream_t ws = side ? ctx->side : s;
+  // bf16: the q/k/v and out weight gradients as one paired launch when their 256 x 256 tiles
+  // together make a whole round of the CUs (d32: 192 + 64 of 256); a function of the shape, so
+  // the results do not depend on the streams
+  bool pair_wgrads = false;
+  if (std::is_same<T, bf16>::value) {
+    const long long t_qkv = cdiv(3LL * D, 256) * cdiv((long long)D, 256);
+    const long long t_out = cdiv((long long)D, 256) * cdiv((long long)D, 256);
+    pair_wgrads = t_qkv % 8 == 0 && t_qkv + t_out == (long long)gemm_detail::resident_cus();
+  }
   auto fork = [&]() -> gpt_status {
     if (!side) return GPT_OK;
     if (hipEventRecord(ctx->fork, s) != hipSuccess || hipStreamWaitEvent(ws, ctx->fork, 0) != hipSuccess)
@@ -398,12 +407,14 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
     STAGE("rmsnorm_bwd", 0, ND * (16 + es) + 4.0 * N,
           launch_rms_bwd<T>(b.x_mid, b.rstd_b, p.db, p.dx, p.dx, dx_t, N, D, s));
     // attention: x_mid = x_in + O Wo^T
-    TRY(fork());
-    SIDE_STAGE("out_wgrad", mm(D, D, N), 0,
-               gemm_wgrad<G_OUT_WGRAD, T>(false, false, D, D, (int)N, dx_t, D, o, D,
-                                          EpiStoreF32{G + Ly.wo[l], D, beta}, p.splitk,
-                                          p.splitk_floats, ws));
-    TRY(mark(ctx->ev_ow));
+    if (!pair_wgrads) {
+      TRY(fork());
+      SIDE_STAGE("out_wgrad", mm(D, D, N), 0,
+                 gemm_wgrad<G_OUT_WGRAD, T>(false, false, D, D, (int)N, dx_t, D, o, D,
+                                            EpiStoreF32{G + Ly.wo[l], D, beta}, p.splitk,
+                                            p.splitk_floats, ws));
+      TRY(mark(ctx->ev_ow));
+    }
     STAGE("out_dgrad", mm(N, D, D), 0,
           gemm<G_OUT_DGRAD, T>(true, false, (int)N, D, D, dx_t, D, P + Ly.wo[l], D,
                                EpiStore<T>{dO, D}, s));
@@ -416,11 +427,24 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
     if (vadd)
       STAGE("dvadd_accum", 0, ND * (es + (l != Lc - 1 ? 8 : 4)),
             launch_accum_rows<T>(p.dU, dqkv + 2 * D, 3LL * D, N, D, l != Lc - 1, s));
-    TRY(fork());
-    SIDE_STAGE("qkv_wgrad", mm(3 * D, D, N), 0,
-               gemm_wgrad<G_QKV_WGRAD, T>(false, false, 3 * D, D, (int)N, dqkv, 3 * D, a, D,
-                                          EpiStoreF32{G + Ly.wqkv[l], D, beta}, p.splitk,
-                                          p.splitk_floats, ws));
+    if (pair_wgrads) {
+      // the out weight gradient waits for the q/k/v one: together their 256 x 256 tiles fill
+      // one round of the CUs (dx_t, which the out product reads, is rewritten only below)
+      TRY(fork());
+      if constexpr (std::is_same<T, bf16>::value)
+        SIDE_STAGE("qkv_out_wgrad", mm(3 * D, D, N) + mm(D, D, N), 0,
+                   gemm_wgrad_pair<G_QKV_OUT_WGRAD>(3 * D, D, (int)N, dqkv, 3 * D, a, D,
+                                                    EpiStoreF32{G + Ly.wqkv[l], D, beta}, D, D,
+                                                    (int)N, dx_t, D, o, D,
+                                                    EpiStoreF32{G + Ly.wo[l], D, beta}, ws));
+      TRY(mark(ctx->ev_ow));
+    } else {
+      TRY(fork());
+      SIDE_STAGE("qkv_wgrad", mm(3 * D, D, N), 0,
+                 gemm_wgrad<G_QKV_WGRAD, T>(false, false, 3 * D, D, (int)N, dqkv, 3 * D, a, D,
+                                            EpiStoreF32{G + Ly.wqkv[l], D, beta}, p.splitk,
+                                            p.splitk_floats, ws));
+    }
     STAGE("qkv_dgrad", mm(N, D, 3 * D), 0,
           gemm<G_QKV_DGRAD, T>(true, false, (int)N, D, 3 * D, dqkv, 3 * D, P + Ly.wqkv[l], D,
                                EpiStoreF32{p.db, D, 0}, s));

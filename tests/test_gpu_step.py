@@ -190,18 +190,22 @@ def test_gpt2_small_bf16_full_launch_sampled_sequences():
     assert B.gpt_check_errors(step.ctx) == 0        # no kernel wrote past its buffer
 
 
-@pytest.mark.parametrize("base", ["speedrun-bf16", "d32-small-batch"])
+@pytest.mark.parametrize("base", ["speedrun-bf16", "d32-small-batch", "small-chunked"])
 def test_weight_gradient_stream_changes_no_bit(base):
     """The blocks' weight-gradient products on a stream of their own give bitwise the results of
     the same step on the caller's stream alone: two micro-batches (overwrite, then accumulate
     with grad_scale 1/2), loss, every gradient and the addend gradients compared bit for bit.
     Shapes: the speedrun micro-batch (GPT-2-small with both table addends and the trigram
-    projection, full 8 x 1024 launch) and the d32 layer shapes with 4 layers and 2 x 2048
-    tokens."""
+    projection, full 8 x 1024 launch), the d32 layer shapes with 4 layers and 2 x 2048 tokens,
+    and a small model whose LM head and cross-entropy run in four chunks (the last ragged)."""
     if base == "speedrun-bf16":
         cfg = configs.SPEEDRUN
-    else:
+    elif base == "d32-small-batch":
         cfg = configs.D32.replace(n_layer=4, batch=2)
+    else:
+        cfg = configs.GPTConfig(n_layer=2, d_model=256, n_head=4, head_dim=64, d_mlp=1024,
+                                vocab=4096, seq_len=128, batch=5, dtype=configs.BF16,
+                                ce_chunk_tokens=192, has_v_add=1)
     params = inputs.model_params(cfg, 106)
     N, D = cfg.tokens, cfg.d_model
     vadd = cfg.has_v_add or cfg.has_trigram
