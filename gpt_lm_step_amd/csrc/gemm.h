@@ -22,9 +22,11 @@
 //  * epilogues are fused: bf16/fp32 stores, value addend, rotary + QK-norm (EpiQKVRope), ReLU^2,
 //    dReLU^2, residual add, beta-accumulation, split-K partials, Newton-Schulz combinations;
 //  * blocks are dispatched round-robin over the 8 XCDs; each XCD walks a contiguous range of
-//    tiles in groups of 8 row tiles (operand panels shared in its L2);
+//    tiles in groups of 4 row tiles (operand panels shared in its L2);
 //  * shapes whose tiling leaves CUs idle and that have an fp32 output (weight gradients, the LM
-//    head's input gradient) split K into fp32 partials reduced in split order (deterministic).
+//    head's input gradient) split K into fp32 partials reduced in split order (deterministic);
+//  * two independent weight gradients whose tiles together make one round of the CUs can run as
+//    one paired launch (gemm_wgrad_pair).
 // fp32 (gemm_kernel, the parity configurations only): 64 x 64 tiles staged through registers.
 // Header-only: every call site instantiates its own kernel symbol (a GemmSite tag), so
 // profiles name the projection a launch belongs to.

@@ -64,10 +64,6 @@ gpt_status validate(const gpt_config* c) {
 
 namespace {
 
-
-// Tokens of one head/cross-entropy chunk: the caller's choice, capped so that the bf16/fp32
-// logits chunk spans at most 2 GiB (the most one GEMM operand may span); by default all tokens
-// when they fit.
 // Whether the blocks' weight gradients get a stream of their own (bf16 path only): the caller's
 // choice, else where the MLP-up weight gradient's plan uses 128 x 128 tiles (two workgroups per
 // CU, so the products of both streams share the CUs).  Measured on MI355X: GPT-2-small step
@@ -80,6 +76,9 @@ bool use_wgrad_stream(const gpt_config& c) {
   return !gemm_detail::split_plan(c.d_mlp, c.d_model, (int)n).big;
 }
 
+// Tokens of one head/cross-entropy chunk: the caller's choice, capped so that the bf16/fp32
+// logits chunk spans at most 2 GiB (the most one GEMM operand may span); by default all tokens
+// when they fit.
 long long ce_chunk_rows(const gpt_config& c) {
   const long long N = (long long)c.batch * c.seq_len;
   const long long esz = c.dtype == GPT_BF16 ? 2 : 4;
@@ -242,8 +241,8 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
   };
   // The blocks' weight gradients go to ws (the side stream, or s itself): fork() makes ws wait
   // for everything issued to s so far; mark(e) records e after what ws holds so far, and
-  // await_mark(e) makes s wait for it.
-  // (a profiled step stays on one stream, so that each stage's events time its own kernels)
+  // await_mark(e) makes s wait for it.  A profiled step stays on one stream, so that each
+  // stage's events time its own kernels.
   const bool side = ctx->side != nullptr && !prof.on;
   hipStream_t ws = side ? ctx->side : s;
   // bf16: the q/k/v and out weight gradients as one paired launch when their 256 x 256 tiles
@@ -428,8 +427,9 @@ gpt_status run_step(gpt_ctx* ctx, const int32_t* tokens, const int32_t* targets,
       STAGE("dvadd_accum", 0, ND * (es + (l != Lc - 1 ? 8 : 4)),
             launch_accum_rows<T>(p.dU, dqkv + 2 * D, 3LL * D, N, D, l != Lc - 1, s));
     if (pair_wgrads) {
-      // the out weight gradient waits for the q/k/v one: together their 256 x 256 tiles fill
-      // one round of the CUs (dx_t, which the out product reads, is rewritten only below)
+      // the out weight gradient, deferred to here, runs in one launch with the q/k/v one:
+      // together their 256 x 256 tiles fill one round of the CUs (dx_t, which the out product
+      // reads, is rewritten only by the norm backward below)
       TRY(fork());
       if constexpr (std::is_same<T, bf16>::value)
         SIDE_STAGE("qkv_out_wgrad", mm(3 * D, D, N) + mm(D, D, N), 0,
