@@ -225,6 +225,22 @@ def test_weight_gradient_stream_changes_no_bit(base):
         if vadd:
             assert torch.equal(a.d_v, b.d_v), mb
     assert torch.isfinite(steps[0].grads).all()
+    # accumulating a micro-batch onto its own gradient doubles it exactly (x + x is exact in
+    # fp32, and every kernel repeats its arithmetic bit for bit): the accumulate epilogues, the
+    # paired launch's included, add the stored value once.  A chunked LM head sums its chunks'
+    # weight gradients into the stored one, so there the doubling holds to rounding only.
+    st = steps[0]
+    tok = inputs.step_tokens(cfg, 40)
+    st.run(tok, tok[:, 1:], *adds, grad_scale=0.5, accumulate=0)
+    once = st.grad_dict()
+    st.run(tok, tok[:, 1:], *adds, grad_scale=0.5, accumulate=1)
+    twice = st.grad_dict()
+    chunked = 0 < cfg.ce_chunk_tokens < cfg.tokens
+    for name, g in once.items():
+        if chunked and name == "lm_head":
+            assert rel_l2(twice[name], 2 * g) <= 1e-6, name
+        else:
+            assert np.array_equal(twice[name], 2 * g), name
 
 
 @pytest.mark.timeout(900)
